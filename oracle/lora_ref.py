@@ -1,0 +1,83 @@
+"""The plain definition of the mixed-adapter LoRA projection, in float64.
+
+Source: "two 27B models on a single RTX 5090" (blog.kvit.app).
+  * Section 3, weights figure: each changed matrix of the adapted model is the
+    base matrix plus a rank-256 product, W_clef = W_qwen + B.A, with A of shape
+    r x K and B of shape N x r.
+  * Section 4, request-path figure: a request that names the adapter runs, in
+    each changed matrix, the base product plus the output of the adapter's two
+    thin matrices applied in turn; a request that names the base model uses the
+    base weights alone; both kinds of request share one batch.
+
+So, for a token row x of a request naming adapter a (s is the call's scale,
+1.0 for the pages' unscaled merge):
+
+    y = x W^T + s * ((x A_a^T) B_a^T)
+
+and for every other row y = x W^T.  The rows of one request are contiguous:
+segment g covers rows [seg_starts[g], seg_starts[g+1]) and seg_adapter[g] is
+its adapter index, or -1 for the base weights alone.
+
+The oracle computes exactly this in float64, one segment at a time, with the
+adapter term formed in the order the pages give (shrink by A, then expand by
+B).  Inputs are the exact values of the stored elements (bf16 or fp32, widened
+to float64 without change); the result stays in float64.  Matrix products use
+numpy's float64 matmul as a library step.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def validate_segments(seg_starts, seg_adapter, M: int, n_adapters: int):
+    """Check that the segments tile rows [0, M) in order and name valid adapters."""
+    s = np.asarray(seg_starts, dtype=np.int64)
+    a = np.asarray(seg_adapter, dtype=np.int64)
+    if s.ndim != 1 or a.ndim != 1 or len(s) != len(a) + 1:
+        raise ValueError("seg_starts must have one more entry than seg_adapter")
+    if M > 0 and len(a) == 0:
+        raise ValueError("a non-empty batch needs at least one segment")
+    if len(a) == 0:
+        return s, a
+    if s[0] != 0 or s[-1] != M or np.any(np.diff(s) < 0):
+        raise ValueError("segments must start at 0, never go backwards and end at M")
+    if np.any(a < -1) or np.any(a >= n_adapters):
+        raise ValueError("adapter index out of range")
+    return s, a
+
+
+def lora_proj_ref(X, seg_starts, seg_adapter, W, A, B, scale, rows=None) -> np.ndarray:
+    """Y = X W^T, plus s (X A_a^T) B_a^T on the rows of segments naming adapter a.
+
+    X: (M, K), W: (N, K), A: list of (r, K), B: list of (N, r) — exact input
+    values (any float dtype).  rows: optional global row indices; only those
+    rows of Y are computed (rows are independent of one another).
+    Returns float64 of shape (len(rows), N).
+    """
+    X = np.asarray(X)
+    M, K = X.shape
+    W64 = np.asarray(W, dtype=np.float64)
+    N = W64.shape[0]
+    if W64.shape[1] != K:
+        raise ValueError("W must be N x K")
+    s, a = validate_segments(seg_starts, seg_adapter, M, len(A))
+    rows = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
+    Y = np.empty((len(rows), N), dtype=np.float64)
+    if len(rows) == 0:
+        return Y
+    seg_of_row = np.searchsorted(s, rows, side="right") - 1
+    for g in np.unique(seg_of_row):
+        pos = np.nonzero(seg_of_row == g)[0]
+        x = X[rows[pos]].astype(np.float64)
+        base = x @ W64.T
+        adapter = int(a[g])
+        if adapter < 0:
+            Y[pos] = base
+            continue
+        A64 = np.asarray(A[adapter], dtype=np.float64)
+        B64 = np.asarray(B[adapter], dtype=np.float64)
+        if A64.shape[1] != K or B64.shape[0] != N or A64.shape[0] != B64.shape[1]:
+            raise ValueError("A must be r x K and B must be N x r")
+        t = x @ A64.T                  # the first thin matrix: r values per row
+        Y[pos] = base + float(scale) * (t @ B64.T)   # the second, added to the base
+    return Y
