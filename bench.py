@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Throughput of the mixed-adapter LoRA projection on one MI355X.
+
+One step is one pass of the whole hot path — segment scheduling, shrink,
+fused base product + expand, bf16 store — over every projection of the
+workload, with all inputs already resident in HBM:
+
+  prefill16k (the headline): one adapted layer, 16,384 token rows that all
+      name the adapter, seven projections (q, k, v, o 5120->5120; gate, up
+      5120->17408; down 17408->5120), rank 256.  Reported in TFLOP/s and as a
+      fraction of the bf16 MFMA peak.
+  suffix (decode line): 24 adapted layers x 7 projections, 64 adapter rows plus
+      6 base-only decode rows (M = 70).  Reported in GB/s and as a fraction of
+      HBM bandwidth.
+
+Algorithmic work per call: FLOP = 2 M N K + 2 M_a r (K + N); bytes = W + X + Y,
+plus A_a and B_a when the call has adapter rows (bf16).
+
+The output kernel (base product + expand + store) is timed on its own with HIP
+events recorded around every launch inside the timed region; its achieved rate
+is the roofline figure.  The CPU baseline times the fp64 oracle on a bounded
+sample of rows of the same workload.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from rank_adapted_gemm_amd import binding as bd  # noqa: E402
+from rank_adapted_gemm_amd import synth  # noqa: E402
+
+METRIC = "TFLOP/s + %MFMA peak (16k prefill); GB/s + %HBM peak (decode batch)"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCE = os.path.join(ROOT, "rank_adapted_gemm_amd", "csrc", "lora_bf16.hip")
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------------ HIP events
+class HipEvents:
+    """hipEvent_t pairs through the HIP runtime (the output kernel is timed on its own stream)."""
+
+    def __init__(self):
+        self.lib = bd.load()      # resolves to the process's one HIP runtime (torch's)
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.events = []
+
+    def pair(self):
+        a, b = ctypes.c_void_p(), ctypes.c_void_p()
+        for e in (a, b):
+            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.events.append(e)
+        return a.value, b.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        if self.lib.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b)) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def close(self):
+        for e in self.events:
+            self.lib.hipEventDestroy(e)
+        self.events = []
+
+
+# ------------------------------------------------------------------ work model
+def adapter_rows(seg_starts, seg_adapter):
+    s = np.asarray(seg_starts)
+    return int(sum(s[g + 1] - s[g] for g in range(len(seg_adapter)) if seg_adapter[g] >= 0))
+
+
+def call_work(M, Ma, N, K, r):
+    """(main-kernel flops, shrink flops, algorithmic bytes) of one projection call."""
+    main = 2 * M * N * K + 2 * Ma * N * r
+    shrink = 2 * Ma * r * K
+    byts = 2 * (N * K + M * K + M * N + ((r * K + N * r) if Ma else 0))
+    return main, shrink, byts
+
+
+# ------------------------------------------------------------------ device workloads
+def device_layer(cfg, layer, M, dev):
+    """Inputs of one adapted layer drawn on the device (same shapes and sigmas as the host recipe)."""
+    xs = {K: synth.device_normal_bf16((M, K), 1.0, synth.seed_of(cfg, layer, proj, synth.T_X), dev)
+          for K, proj in ((5120, synth.X_NARROW), (17408, synth.X_WIDE))}
+    projs = []
+    for pi, (name, K, N) in enumerate(synth.PROJECTIONS):
+        W = synth.device_normal_bf16((N, K), synth.SIGMA_WAB, synth.seed_of(cfg, layer, pi, synth.T_W), dev)
+        A = synth.device_normal_bf16((synth.RANK, K), synth.SIGMA_WAB, synth.seed_of(cfg, layer, pi, synth.T_A), dev)
+        B = synth.device_normal_bf16((N, synth.RANK), synth.SIGMA_WAB, synth.seed_of(cfg, layer, pi, synth.T_B), dev)
+        projs.append(dict(name=name, K=K, N=N, X=xs[K], W=W, A=A, B=B))
+    return projs
+
+
+class StepRunner:
+    """All calls of one step over preallocated outputs and one shared workspace."""
+
+    def __init__(self, layers, seg_starts, seg_adapter, scale, dev):
+        import torch
+        self.calls = []
+        M = layers[0][0]["X"].shape[0]
+        self.M, self.Ma = M, adapter_rows(seg_starts, seg_adapter)
+        self.seg_starts, self.seg_adapter, self.scale = list(seg_starts), list(seg_adapter), scale
+        ws = max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK) for p in layers[0])
+        self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
+        self.outs = {}
+        for projs in layers:
+            for p in projs:
+                key = (p["N"],)
+                if key not in self.outs:     # outputs of equal shape are reused across layers
+                    self.outs[key] = torch.empty((M, p["N"]), dtype=torch.bfloat16, device=dev)
+                self.calls.append(p)
+        self.stream = torch.cuda.current_stream(dev).cuda_stream
+
+    def work(self):
+        main = shrink = byts = 0
+        for p in self.calls:
+            a, b, c = call_work(self.M, self.Ma, p["N"], p["K"], synth.RANK)
+            main, shrink, byts = main + a, shrink + b, byts + c
+        return main, shrink, byts
+
+    def step(self, events=None):
+        ws = self.workspace
+        for i, p in enumerate(self.calls):
+            st = bd.lora_proj_raw(p["X"].data_ptr(), self.seg_starts, self.seg_adapter, p["W"].data_ptr(),
+                                  [p["A"].data_ptr()], [p["B"].data_ptr()], synth.RANK, self.scale,
+                                  self.outs[(p["N"],)].data_ptr(), self.M, p["N"], p["K"], "bf16",
+                                  ws.data_ptr(), ws.numel(), self.stream,
+                                  None if events is None else events[i])
+            if st != bd.LORA_OK:
+                raise bd.LoraError(st, bd.status_string(st))
+
+
+def time_steps(runner, steps, warmup, hip):
+    import torch
+    for _ in range(warmup):
+        runner.step()
+    torch.cuda.synchronize()
+    pairs = [[hip.pair() for _ in runner.calls] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(steps):
+        runner.step(events=pairs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    main_ms = [[hip.elapsed_ms(a, b) for (a, b) in row] for row in pairs]
+    return wall, np.array(main_ms)
+
+
+# ------------------------------------------------------------------ CPU baseline
+def cpu_baseline(rows: int):
+    """fp64 oracle on `rows` token rows of each prefill16k projection (host recipe weights)."""
+    from oracle import lora_proj_ref
+    try:
+        import threadpoolctl
+        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
+    except Exception:
+        threads = os.cpu_count() or 1
+    g = np.random.Generator(np.random.PCG64(7))
+    total_s = 0.0
+    flops = 0
+    for pi, (name, K, N) in enumerate(synth.PROJECTIONS):
+        (_, Wf), (_, Af), (_, Bf) = synth.projection_weights(2, 0, pi, K, N)
+        Xs = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(g.standard_normal((rows, K), dtype=np.float32)))
+        t0 = time.perf_counter()
+        lora_proj_ref(Xs, [0, rows], [0], Wf, [Af], [Bf], 1.0)
+        total_s += time.perf_counter() - t0
+        main, shrink, _ = call_work(rows, rows, N, K, synth.RANK)
+        flops += main + shrink
+        log(f"  cpu oracle {name}: {rows} rows")
+    return dict(value=flops / total_s / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+                sample=f"{rows} of 16384 rows of each of the 7 prefill16k projections, fp64 numpy oracle; "
+                       f"{flops / 1e9:.1f} GFLOP in {total_s:.1f} s")
+
+
+def traffic_record():
+    """HBM bytes per output-kernel launch from the committed rocprofv3 counter runs, if current."""
+    try:
+        rec = json.load(open(TRAFFIC_FILE))
+        src = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") == src:
+            return rec.get("bytes_per_launch")
+    except (OSError, ValueError):
+        pass
+    return None
+
+
+# ------------------------------------------------------------------ main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: the projection is measured at one GPU's share "
+              f"(requested --gpus {a.gpus}); rows shard across GPUs without any exchange.", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-process; do not launch it with several ranks", file=sys.stderr)
+        return 2
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    bd.load()
+    hip = HipEvents()
+
+    # ---------------- prefill16k
+    w = synth.WORKLOADS["prefill16k"]
+    log("prefill16k: drawing inputs on the device")
+    layer = device_layer(w["cfg"], 0, w["M"], dev)
+    runner = StepRunner([layer], w["seg_starts"], w["seg_adapter"], w["scale"], dev)
+    main_flops, shrink_flops, byts = runner.work()
+    log(f"prefill16k: {a.warmup} warmup + {a.steps} timed steps of {len(runner.calls)} calls")
+    wall, main_ms = time_steps(runner, a.steps, a.warmup, hip)
+    ms_per_step = wall * 1e3 / a.steps
+    step_flops = main_flops + shrink_flops
+    value = step_flops / (ms_per_step / 1e3) / 1e12
+    main_achieved = main_flops * a.steps / (main_ms.sum() / 1e3) / 1e12
+    per_proj_ms = main_ms.mean(axis=0)
+    log(f"prefill16k: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s; "
+        + ", ".join(f"{p['name']} {t:.3f}" for p, t in zip(runner.calls, per_proj_ms)))
+    traffic = traffic_record()
+    roofline = dict(bound="mfma", achieved=round(main_achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
+                    frac=round(main_achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
+                    kernel="main_kernel<Tile<256,256,2,2>, bf16 out>",
+                    launch_avg_ms=round(float(main_ms.mean()), 4),
+                    per_projection_ms={p["name"]: round(float(t), 4) for p, t in zip(runner.calls, per_proj_ms)})
+    del runner, layer
+    torch.cuda.empty_cache()
+
+    # ---------------- suffix decode stack
+    decode = None
+    if not a.no_decode:
+        w5 = synth.WORKLOADS["suffix"]
+        log("suffix: drawing 24 layers on the device")
+        layers = [device_layer(w5["cfg"], l, w5["M"], dev) for l in range(w5["layers"])]
+        runner = StepRunner(layers, w5["seg_starts"], w5["seg_adapter"], w5["scale"], dev)
+        dmain, dshrink, dbytes = runner.work()
+        wall5, main5 = time_steps(runner, a.decode_steps, a.warmup, hip)
+        ms5 = wall5 * 1e3 / a.decode_steps
+        gbs = dbytes / (ms5 / 1e3) / 1e9
+        decode = dict(workload="suffix: 24 layers x 7 projections, 64 adapter rows + 6 base-only decode rows, r=256",
+                      value=round(gbs, 1), unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                      ms_per_step=round(ms5, 4), bytes_per_step=dbytes, steps=a.decode_steps,
+                      tflops=round((dmain + dshrink) / (ms5 / 1e3) / 1e12, 2),
+                      output_kernel_avg_ms=round(float(main5.mean()), 5))
+        log(f"suffix: {ms5:.3f} ms/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+        del runner, layers
+        torch.cuda.empty_cache()
+    hip.close()
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        log("cpu baseline: fp64 oracle on sampled rows")
+        cpu = cpu_baseline(a.cpu_rows)
+
+    out = dict(metric=METRIC, value=round(value, 2), unit="TFLOP/s", n_gpus=1, steps=a.steps, warmup=a.warmup,
+               ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+               dtype="bf16", data="synthetic",
+               config=dict(workload="prefill16k: one adapted layer, 16384 rows all naming the adapter, "
+                                    "7 projections (q,k,v,o 5120->5120; gate,up 5120->17408; down 17408->5120), "
+                                    "rank 256, s=1",
+                           M=w["M"], rank=synth.RANK, flop_per_step=step_flops, bytes_per_step=byts,
+                           parallelism="single GPU"),
+               roofline=roofline, cpu_baseline=cpu, decode=decode)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

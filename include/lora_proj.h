@@ -1,0 +1,149 @@
+/*
+ * lora_proj.h — the mixed-adapter LoRA projection on AMD MI355X (gfx950).
+ *
+ * What it computes ("two 27B models on a single RTX 5090", section 3 weights
+ * figure and section 4 request-path figure): each changed matrix of the adapted
+ * model equals the base matrix plus a rank-r product B.A, and a request that
+ * names the adapter runs the base product plus the adapter's two thin matrices,
+ * while requests that name the base model use the base weights alone, in the
+ * same batch.  With s the call's scale (1.0 reproduces the unscaled merge):
+ *
+ *     Y[m,:] = X[m,:] W^T + s (X[m,:] A_a^T) B_a^T   rows of a segment naming adapter a
+ *     Y[m,:] = X[m,:] W^T                            rows of base-only segments
+ *
+ * Layout.  Every matrix is dense and row-major with the reduction index
+ * contiguous (the nn.Linear weight layout): X is M x K, W is N x K, A_a is
+ * r x K, B_a is N x r, Y is M x N.  Rows are packed (leading dimension = row
+ * length).  Device pointers must be 16-byte aligned.
+ *
+ * Segments.  The rows of one request are contiguous.  Segment g covers rows
+ * [seg_starts[g], seg_starts[g+1]); seg_adapter[g] is -1 (base-only) or an
+ * adapter index in [0, n_adapters).  seg_starts[0] == 0, entries never
+ * decrease, seg_starts[n_seg] == M.  Empty segments are allowed.
+ *
+ * Precision.  LORA_BF16: bf16 inputs and output, fp32 accumulation, the
+ * intermediate X A^T held at fp32-equivalent precision, one round-to-nearest-
+ * even to bf16 at the store.  LORA_BF16_F32OUT: the same kernels with an fp32
+ * store.  LORA_F32: fp32 inputs and output (test mode, not tuned for speed).
+ *
+ * Streams and ownership.  Calls are asynchronous on `stream` and return once
+ * the work is enqueued.  The caller owns every buffer: device buffers must stay
+ * valid until the stream work completes; host arrays (seg_starts, seg_adapter,
+ * A, B) may be released as soon as the call returns.  The library allocates no
+ * memory per call and keeps no state between calls; it never prints, aborts or
+ * falls back to another path.  Concurrent calls need separate workspaces and
+ * outputs.
+ *
+ * Errors.  Every argument is checked on the host before anything is launched;
+ * on error the call returns the code, launches nothing and leaves Y untouched.
+ * A failed launch returns LORA_EHIP; faults during execution surface at the
+ * caller's next synchronisation.  M == 0 is a successful no-op.
+ */
+#ifndef LORA_PROJ_H
+#define LORA_PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum lora_status {
+  LORA_OK = 0,
+  LORA_EINVAL = 1,        /* null pointer, negative or inconsistent size, misalignment, Y overlapping an input */
+  LORA_ESEGMENTS = 2,     /* segment table malformed */
+  LORA_EADAPTER = 3,      /* adapter index out of range, or its A/B pointer is null */
+  LORA_EUNSUPPORTED = 4,  /* shape, rank, dtype or table size outside the documented limits */
+  LORA_EWORKSPACE = 5,    /* workspace missing or smaller than lora_proj_workspace_bytes() */
+  LORA_EHIP = 6           /* the HIP runtime reported an error while enqueueing */
+} lora_status;
+
+typedef enum lora_dtype {
+  LORA_BF16 = 0,          /* bf16 X, W, A, B and Y */
+  LORA_F32 = 1,           /* fp32 X, W, A, B and Y (test mode) */
+  LORA_BF16_F32OUT = 2    /* bf16 X, W, A, B; fp32 Y */
+} lora_dtype;
+
+/* Documented limits (checked; anything beyond returns LORA_EUNSUPPORTED):
+ *   - at most LORA_MAX_SEGMENTS segments once empty segments are dropped and neighbours
+ *     naming the same adapter are merged;
+ *   - n_adapters <= LORA_MAX_ADAPTERS;
+ *   - rank a multiple of 16 in [LORA_MIN_RANK, LORA_MAX_RANK] when any row names an adapter;
+ *   - K a multiple of 8;
+ *   - every operand (X, W, each A_a and B_a, Y, the used workspace) smaller than 2 GiB. */
+#define LORA_MAX_SEGMENTS 256
+#define LORA_MAX_ADAPTERS 32
+#define LORA_MIN_RANK 16
+#define LORA_MAX_RANK 512
+
+/*
+ * lora_proj — one projection call over a batch of rows from several requests.
+ *
+ *   X            device, M x K (dtype's input type)
+ *   seg_starts   HOST, n_seg + 1 int32
+ *   seg_adapter  HOST, n_seg int32, -1 or 0 .. n_adapters-1
+ *   n_seg        number of segments (>= 1 when M > 0)
+ *   W            device, N x K
+ *   A            HOST array of n_adapters device pointers, each r x K (entries may be
+ *                NULL for adapters no non-empty segment names)
+ *   B            HOST array of n_adapters device pointers, each N x r
+ *   n_adapters   0 .. LORA_MAX_ADAPTERS
+ *   rank         r, shared by all adapters of the call (ignored when no row names an adapter)
+ *   scale        s, applied to the adapter term of every adapter row
+ *   Y            device, M x N, fully overwritten; must not overlap X, W, any A/B or the workspace
+ *   workspace    device scratch of at least lora_proj_workspace_bytes(M, N, K, rank, dtype)
+ *                bytes (may be NULL with size 0 when no row names an adapter); its contents
+ *                are not preserved
+ *   stream       HIP stream the work is ordered on (0 = the null stream)
+ */
+lora_status lora_proj(const void* X,
+                      const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                      const void* W,
+                      const void* const* A, const void* const* B,
+                      int32_t n_adapters, int32_t rank, float scale,
+                      void* Y,
+                      int64_t M, int64_t N, int64_t K,
+                      lora_dtype dtype,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream);
+
+/*
+ * lora_proj_ex — lora_proj with two optional timing events.
+ *
+ * Identical arguments, checks and results; in addition, when main_start or
+ * main_stop is not NULL it is recorded on `stream` at the start / end of the
+ * output kernel (the base product with the adapter expand and the store),
+ * which is the call's dominant kernel, so that it can be timed on its own.
+ * The events belong to the caller and must have been created on the current
+ * device.
+ */
+lora_status lora_proj_ex(const void* X,
+                         const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                         const void* W,
+                         const void* const* A, const void* const* B,
+                         int32_t n_adapters, int32_t rank, float scale,
+                         void* Y,
+                         int64_t M, int64_t N, int64_t K,
+                         lora_dtype dtype,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream,
+                         hipEvent_t main_start, hipEvent_t main_stop);
+
+/* Workspace bytes lora_proj needs for any segment table of this shape (an upper bound).
+ * Returns 0 for invalid arguments. */
+size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype);
+
+/* Name of the kernel path lora_proj takes for this shape: "prefill", "decode" or "f32"
+ * ("invalid" for arguments lora_proj would reject).  A pure function of its arguments. */
+const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype);
+
+/* Static description of a status code; never NULL. */
+const char* lora_status_string(lora_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LORA_PROJ_H */

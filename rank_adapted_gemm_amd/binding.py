@@ -1,0 +1,132 @@
+"""ctypes binding of liblora_proj.so — argument marshalling only.
+
+Every step of the projection runs in the library's HIP kernels.  PyTorch is
+used for device memory and streams: tensors hand over their data pointers and
+the current stream.  If the library is not built, the first call raises; there
+is no other path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "liblora_proj.so")
+
+LORA_OK, LORA_EINVAL, LORA_ESEGMENTS, LORA_EADAPTER, LORA_EUNSUPPORTED, LORA_EWORKSPACE, LORA_EHIP = range(7)
+STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESEGMENTS", 3: "LORA_EADAPTER",
+                4: "LORA_EUNSUPPORTED", 5: "LORA_EWORKSPACE", 6: "LORA_EHIP"}
+DTYPES = {"bf16": 0, "f32": 1, "bf16_f32out": 2}
+MAX_SEGMENTS, MAX_ADAPTERS, MIN_RANK, MAX_RANK = 256, 32, 16, 512
+EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_workspace_bytes", "lora_proj_path", "lora_status_string")
+
+_lib = None
+
+
+class LoraError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+def load():
+    """Load the library (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m rank_adapted_gemm_amd.build`")
+    # PyTorch ships its own copy of the HIP runtime with the same soname as the
+    # system one.  Importing torch first makes the library bind to that copy;
+    # loading the library first would map a second HIP runtime into the
+    # process once torch is imported, and the two would share no state.
+    import torch  # noqa: F401
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    lib.lora_proj.argtypes = [vp, i32p, i32p, i32, vp, ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32,
+                              ctypes.c_float, vp, i64, i64, i64, ctypes.c_int, vp, sz, vp]
+    lib.lora_proj.restype = ctypes.c_int
+    lib.lora_proj_ex.argtypes = lib.lora_proj.argtypes + [vp, vp]
+    lib.lora_proj_ex.restype = ctypes.c_int
+    lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, ctypes.c_int]
+    lib.lora_proj_workspace_bytes.restype = sz
+    lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
+    lib.lora_proj_path.restype = ctypes.c_char_p
+    lib.lora_status_string.argtypes = [ctypes.c_int]
+    lib.lora_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def status_string(status: int) -> str:
+    return load().lora_status_string(status).decode()
+
+
+def workspace_bytes(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> int:
+    return int(load().lora_proj_workspace_bytes(M, N, K, rank, DTYPES[dtype]))
+
+
+def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:
+    return load().lora_proj_path(M, N, K, rank, DTYPES[dtype]).decode()
+
+
+def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, dtype,
+                  workspace=None, workspace_bytes_=0, stream=None, events=None) -> int:
+    """Call the C entry point with raw device addresses (ints) and host segment lists.
+
+    ``events``: optional (start, stop) hipEvent_t handles recorded around the
+    output kernel (calls lora_proj_ex).  Returns the status code.
+    """
+    lib = load()
+    starts = (ctypes.c_int32 * len(seg_starts))(*[int(v) for v in seg_starts])
+    adapt = (ctypes.c_int32 * max(len(seg_adapter), 1))(*[int(v) for v in seg_adapter])
+    n_ad = len(A)
+    a_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(a) if a else None for a in A])
+    b_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(b) if b else None for b in B])
+    args = (X, starts, adapt, len(seg_adapter), W, a_arr, b_arr, n_ad, int(rank), float(scale), Y,
+            int(M), int(N), int(K), DTYPES[dtype] if isinstance(dtype, str) else int(dtype),
+            workspace, int(workspace_bytes_), stream)
+    if events is not None:
+        return int(lib.lora_proj_ex(*args, events[0], events[1]))
+    return int(lib.lora_proj(*args))
+
+
+def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=None, dtype=None, stream=None,
+              events=None):
+    """Y = X W^T, plus s (X A_a^T) B_a^T on rows of segments naming adapter a.
+
+    X (M, K), W (N, K), A[a] (r, K), B[a] (N, r): contiguous CUDA tensors of one
+    dtype (bfloat16, or float32 for the test mode).  seg_starts / seg_adapter:
+    host sequences of ints.  dtype: "bf16", "f32" or "bf16_f32out" (default
+    from X).  Returns Y (M, N); raises LoraError on a non-OK status.
+    """
+    import torch
+    if dtype is None:
+        dtype = "f32" if X.dtype == torch.float32 else "bf16"
+    in_t = torch.float32 if dtype == "f32" else torch.bfloat16
+    out_t = torch.bfloat16 if dtype == "bf16" else torch.float32
+    tensors = [X, W, *A, *B]
+    for t in tensors:
+        if t.dtype != in_t or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"inputs must be contiguous {in_t} CUDA tensors")
+    M, K = X.shape
+    N = W.shape[0]
+    rank = A[0].shape[0] if len(A) else 0
+    if out is None:
+        out = torch.empty((M, N), dtype=out_t, device=X.device)
+    if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
+    need = workspace_bytes(M, N, K, rank, dtype) if rank else 0
+    if workspace is None and need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device).cuda_stream
+    st = lora_proj_raw(X.data_ptr(), seg_starts, seg_adapter, W.data_ptr(),
+                       [a.data_ptr() for a in A], [b.data_ptr() for b in B], rank, scale,
+                       out.data_ptr(), M, N, K, dtype, ws_ptr, ws_bytes, stream, events)
+    if st != LORA_OK:
+        raise LoraError(st, status_string(st))
+    return out

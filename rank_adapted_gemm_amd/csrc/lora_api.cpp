@@ -1,0 +1,221 @@
+// C-ABI entry points: argument checks, segment scheduling and kernel launches.
+//
+// Scheduling follows the request model of "two 27B models on a single RTX
+// 5090" (section 4): requests naming the adapter and requests naming the base
+// model share one batch, and the adapter applies only to the former.  The host
+// turns the caller's segment table into a compact one (empty segments dropped,
+// neighbours with the same adapter merged) that every kernel receives by value.
+// Row tiles that hold no adapter row skip the shrink and the expand entirely,
+// so base-only rows never read A or B.
+#include <string.h>
+
+#include <algorithm>
+
+#include "lora_internal.h"
+
+namespace {
+
+using lora::AdapterTable;
+using lora::ProjArgs;
+using lora::SegTable;
+
+constexpr int64_t kMaxOperandBytes = int64_t(1) << 31;
+
+size_t in_elem_bytes(lora_dtype d) { return d == LORA_F32 ? 4 : 2; }
+size_t out_elem_bytes(lora_dtype d) { return d == LORA_BF16 ? 2 : 4; }
+bool dtype_ok(int d) { return d == LORA_BF16 || d == LORA_F32 || d == LORA_BF16_F32OUT; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Bytes of the intermediate s X A^T: bf16 hi + lo parts, or fp32 — 4 bytes per
+// element either way, rows indexed by global row.
+size_t t_bytes(int64_t M, int64_t rank) { return size_t(M) * size_t(rank) * 4; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  uintptr_t a0 = reinterpret_cast<uintptr_t>(a), b0 = reinterpret_cast<uintptr_t>(b);
+  return a0 < b0 + nb && b0 < a0 + na;
+}
+
+lora_status check_shape(int64_t M, int64_t N, int64_t K, lora_dtype dtype) {
+  if (!dtype_ok(dtype)) return LORA_EUNSUPPORTED;
+  if (M < 0 || N < 1 || K < 1) return LORA_EINVAL;
+  if (K % 8 != 0) return LORA_EUNSUPPORTED;
+  const int64_t ie = int64_t(in_elem_bytes(dtype)), oe = int64_t(out_elem_bytes(dtype));
+  if (M * K * ie >= kMaxOperandBytes || N * K * ie >= kMaxOperandBytes || M * N * oe >= kMaxOperandBytes)
+    return LORA_EUNSUPPORTED;
+  return LORA_OK;
+}
+
+bool rank_ok(int64_t rank) {
+  return rank >= LORA_MIN_RANK && rank <= LORA_MAX_RANK && rank % 16 == 0;
+}
+
+bool small_m(int64_t M) { return M <= lora::kDecodeMaxRows; }
+
+}  // namespace
+
+extern "C" {
+
+const char* lora_status_string(lora_status s) {
+  switch (s) {
+    case LORA_OK: return "ok";
+    case LORA_EINVAL: return "invalid argument (null pointer, bad size, misalignment or overlapping output)";
+    case LORA_ESEGMENTS: return "malformed segment table";
+    case LORA_EADAPTER: return "adapter index out of range or adapter pointer missing";
+    case LORA_EUNSUPPORTED: return "shape, rank, dtype or table size outside the supported limits";
+    case LORA_EWORKSPACE: return "workspace missing or too small";
+    case LORA_EHIP: return "HIP runtime error while enqueueing";
+  }
+  return "unknown status";
+}
+
+size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype) {
+  if (check_shape(M, N, K, dtype) != LORA_OK || !rank_ok(rank)) return 0;
+  return t_bytes(M, rank);
+}
+
+const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype) {
+  if (check_shape(M, N, K, dtype) != LORA_OK) return "invalid";
+  (void)rank;
+  if (dtype == LORA_F32) return "f32";
+  return small_m(M) ? "decode" : "prefill";
+}
+
+lora_status lora_proj_ex(const void* X,
+                         const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                         const void* W,
+                         const void* const* A, const void* const* B,
+                         int32_t n_adapters, int32_t rank, float scale,
+                         void* Y,
+                         int64_t M, int64_t N, int64_t K,
+                         lora_dtype dtype,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream,
+                         hipEvent_t main_start, hipEvent_t main_stop) {
+  lora_status st = check_shape(M, N, K, dtype);
+  if (st != LORA_OK) return st;
+  if (M == 0) return LORA_OK;
+  if (!X || !W || !Y || !aligned16(X) || !aligned16(W) || !aligned16(Y)) return LORA_EINVAL;
+  if (n_adapters < 0) return LORA_EINVAL;
+  if (n_adapters > LORA_MAX_ADAPTERS) return LORA_EUNSUPPORTED;
+  if (n_adapters > 0 && (!A || !B)) return LORA_EINVAL;
+
+  // ---- segment table: validate, drop empty segments, merge equal neighbours
+  if (!seg_starts || !seg_adapter || n_seg < 1) return LORA_ESEGMENTS;
+  if (seg_starts[0] != 0 || int64_t(seg_starts[n_seg]) != M) return LORA_ESEGMENTS;
+  SegTable tbl;
+  memset(&tbl, 0, sizeof(tbl));
+  tbl.n = 0;
+  bool used[LORA_MAX_ADAPTERS] = {};
+  int64_t adapter_rows = 0;
+  for (int32_t g = 0; g < n_seg; ++g) {
+    const int32_t lo = seg_starts[g], hi = seg_starts[g + 1];
+    if (hi < lo) return LORA_ESEGMENTS;
+    const int32_t a = seg_adapter[g];
+    if (a < -1 || a >= n_adapters) return LORA_EADAPTER;
+    if (hi == lo) continue;
+    if (a >= 0) {
+      used[a] = true;
+      adapter_rows += hi - lo;
+    }
+    if (tbl.n > 0 && tbl.adapter[tbl.n - 1] == a) {
+      tbl.start[tbl.n] = hi;             // extend the previous segment
+      continue;
+    }
+    if (tbl.n == LORA_MAX_SEGMENTS) return LORA_EUNSUPPORTED;
+    tbl.start[tbl.n] = lo;
+    tbl.adapter[tbl.n] = int8_t(a);
+    ++tbl.n;
+    tbl.start[tbl.n] = hi;
+  }
+
+  // ---- adapters named by non-empty segments
+  const bool has_adapter = adapter_rows > 0;
+  const size_t ie = in_elem_bytes(dtype), oe = out_elem_bytes(dtype);
+  AdapterTable at;
+  memset(&at, 0, sizeof(at));
+  const size_t a_bytes = size_t(rank > 0 ? rank : 0) * size_t(K) * ie;
+  const size_t b_bytes = size_t(N) * size_t(rank > 0 ? rank : 0) * ie;
+  if (has_adapter) {
+    if (!rank_ok(rank)) return LORA_EUNSUPPORTED;
+    if (int64_t(a_bytes) >= kMaxOperandBytes || int64_t(b_bytes) >= kMaxOperandBytes) return LORA_EUNSUPPORTED;
+    for (int a = 0; a < n_adapters; ++a) {
+      if (!used[a]) continue;
+      if (!A[a] || !B[a]) return LORA_EADAPTER;
+      if (!aligned16(A[a]) || !aligned16(B[a])) return LORA_EINVAL;
+      at.A[a] = A[a];
+      at.B[a] = B[a];
+    }
+  }
+
+  // ---- workspace
+  const size_t need = has_adapter ? t_bytes(M, rank) : 0;
+  if (need > 0) {
+    if (!workspace || workspace_bytes < need) return LORA_EWORKSPACE;
+    if (!aligned16(workspace)) return LORA_EINVAL;
+    if (int64_t(need) >= kMaxOperandBytes) return LORA_EUNSUPPORTED;
+  }
+
+  // ---- the output may not overlap anything the call reads or the workspace
+  const size_t y_bytes = size_t(M) * size_t(N) * oe;
+  const size_t x_bytes = size_t(M) * size_t(K) * ie;
+  const size_t w_bytes = size_t(N) * size_t(K) * ie;
+  if (overlaps(Y, y_bytes, X, x_bytes) || overlaps(Y, y_bytes, W, w_bytes)) return LORA_EINVAL;
+  if (need > 0 && (overlaps(Y, y_bytes, workspace, need) || overlaps(X, x_bytes, workspace, need) ||
+                   overlaps(W, w_bytes, workspace, need)))
+    return LORA_EINVAL;
+  if (has_adapter) {
+    for (int a = 0; a < n_adapters; ++a) {
+      if (!used[a]) continue;
+      if (overlaps(Y, y_bytes, A[a], a_bytes) || overlaps(Y, y_bytes, B[a], b_bytes)) return LORA_EINVAL;
+      if (overlaps(workspace, need, A[a], a_bytes) || overlaps(workspace, need, B[a], b_bytes))
+        return LORA_EINVAL;
+    }
+  }
+
+  ProjArgs p;
+  p.X = X;
+  p.W = W;
+  p.Y = Y;
+  p.T = has_adapter ? workspace : nullptr;
+  p.M = int32_t(M);
+  p.N = int32_t(N);
+  p.K = int32_t(K);
+  p.rank = has_adapter ? rank : 0;
+  p.scale = scale;
+  p.x_bytes = uint32_t(x_bytes);
+  p.w_bytes = uint32_t(w_bytes);
+  p.y_bytes = uint32_t(y_bytes);
+  p.t_bytes = uint32_t(need);
+  p.a_bytes = uint32_t(a_bytes);
+  p.b_bytes = uint32_t(b_bytes);
+
+  hipError_t e = hipSuccess;
+  if (dtype == LORA_F32) {
+    if (has_adapter) e = lora::launch_f32_shrink(p, tbl, at, stream);
+    if (e == hipSuccess) e = lora::launch_f32_main(p, tbl, at, has_adapter, stream, main_start, main_stop);
+  } else {
+    const bool sm = small_m(M);
+    if (has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, sm, stream);
+    if (e == hipSuccess)
+      e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, sm, stream, main_start,
+                                 main_stop);
+  }
+  return e == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+lora_status lora_proj(const void* X,
+                      const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                      const void* W,
+                      const void* const* A, const void* const* B,
+                      int32_t n_adapters, int32_t rank, float scale,
+                      void* Y,
+                      int64_t M, int64_t N, int64_t K,
+                      lora_dtype dtype,
+                      void* workspace, size_t workspace_bytes,
+                      hipStream_t stream) {
+  return lora_proj_ex(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scale, Y, M, N, K, dtype,
+                      workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"

@@ -1,0 +1,134 @@
+"""Host-side checks of the C-ABI boundary (no GPU needed).
+
+Every call below is rejected during argument checking, before any HIP call,
+so the pointers are placeholders that are never dereferenced.  M == 0 is the
+one accepted call, and it launches nothing.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from rank_adapted_gemm_amd import binding as bd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 1 << 20          # 16-byte aligned placeholder addresses, never dereferenced
+FAKE2, FAKE3, FAKE4, FAKE5 = FAKE * 64, FAKE * 128, FAKE * 192, FAKE * 256
+
+
+def declared_functions():
+    names = []
+    for fn in sorted(os.listdir(os.path.join(ROOT, "include"))):
+        if fn.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", fn)).read()
+            text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+            names += re.findall(r"^[A-Za-z_][\w\s\*]*?\b(lora_\w+)\s*\(", text, flags=re.M)
+    return names
+
+
+def test_library_exports_every_declared_function():
+    lib = bd.load()
+    names = declared_functions()
+    assert set(names) == set(bd.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_one_hip_runtime_in_process():
+    """The library binds to the HIP runtime torch loaded; no second runtime gets mapped."""
+    bd.load()
+    import torch  # noqa: F401
+    maps = {l.split()[-1] for l in open("/proc/self/maps") if "libamdhip64" in l}
+    assert len(maps) == 1, maps
+
+
+def test_limits_match_header():
+    text = open(os.path.join(ROOT, "include", "lora_proj.h")).read()
+    for name, val in (("LORA_MAX_SEGMENTS", bd.MAX_SEGMENTS), ("LORA_MAX_ADAPTERS", bd.MAX_ADAPTERS),
+                      ("LORA_MIN_RANK", bd.MIN_RANK), ("LORA_MAX_RANK", bd.MAX_RANK)):
+        assert re.search(rf"#define {name} {val}\b", text), name
+
+
+def test_status_strings():
+    for s in range(7):
+        assert bd.status_string(s)
+    assert bd.status_string(99) == "unknown status"
+
+
+def test_workspace_and_path_queries():
+    assert bd.workspace_bytes(16384, 5120, 5120, 256) == 16384 * 256 * 4
+    assert bd.workspace_bytes(70, 17408, 5120, 256, "f32") == 70 * 256 * 4
+    assert bd.workspace_bytes(64, 512, 250, 16) == 0          # K not a multiple of 8
+    assert bd.workspace_bytes(64, 512, 256, 24) == 0          # rank not a multiple of 16
+    assert bd.path(16384, 5120, 5120, 256) == "prefill"
+    assert bd.path(70, 5120, 5120, 256) == "decode"
+    assert bd.path(128, 5120, 5120, 256) == "decode"
+    assert bd.path(129, 5120, 5120, 256) == "prefill"
+    assert bd.path(64, 512, 256, 16, "f32") == "f32"
+    assert bd.path(64, 512, 252, 16) == "invalid"
+
+
+def call(**kw):
+    a = dict(X=FAKE, seg_starts=[0, 32, 64], seg_adapter=[-1, 0], W=FAKE2, A=[FAKE3], B=[FAKE4], rank=16,
+             scale=0.5, Y=FAKE5, M=64, N=512, K=256, dtype="bf16", workspace=FAKE * 320,
+             workspace_bytes_=64 * 16 * 4, stream=None)
+    a.update(kw)
+    return bd.lora_proj_raw(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), bd.LORA_EINVAL),
+    (dict(W=None), bd.LORA_EINVAL),
+    (dict(Y=None), bd.LORA_EINVAL),
+    (dict(X=FAKE + 8), bd.LORA_EINVAL),                                  # misaligned
+    (dict(N=0), bd.LORA_EINVAL),
+    (dict(K=0), bd.LORA_EINVAL),
+    (dict(M=-1), bd.LORA_EINVAL),
+    (dict(K=250), bd.LORA_EUNSUPPORTED),                                 # K % 8
+    (dict(dtype=7), bd.LORA_EUNSUPPORTED),
+    (dict(rank=24), bd.LORA_EUNSUPPORTED),                               # rank % 16
+    (dict(rank=528), bd.LORA_EUNSUPPORTED),
+    (dict(rank=0), bd.LORA_EUNSUPPORTED),
+    (dict(M=1 << 20, K=1 << 12, seg_starts=[0, 1 << 20], seg_adapter=[-1]), bd.LORA_EUNSUPPORTED),  # X >= 2 GiB
+    (dict(seg_starts=[1, 32, 64]), bd.LORA_ESEGMENTS),
+    (dict(seg_starts=[0, 32, 63]), bd.LORA_ESEGMENTS),
+    (dict(seg_starts=[0, 40, 32, 64], seg_adapter=[-1, 0, 0]), bd.LORA_ESEGMENTS),
+    (dict(seg_starts=[0], seg_adapter=[]), bd.LORA_ESEGMENTS),            # M > 0 with no segment
+    (dict(seg_adapter=[-1, 1]), bd.LORA_EADAPTER),
+    (dict(seg_adapter=[-2, 0]), bd.LORA_EADAPTER),
+    (dict(A=[None]), bd.LORA_EADAPTER),
+    (dict(B=[None]), bd.LORA_EADAPTER),
+    (dict(A=[FAKE3 + 4]), bd.LORA_EINVAL),
+    (dict(workspace=None, workspace_bytes_=0), bd.LORA_EWORKSPACE),
+    (dict(workspace_bytes_=64 * 16 * 4 - 1), bd.LORA_EWORKSPACE),
+    (dict(Y=FAKE + 4096), bd.LORA_EINVAL),                               # Y overlaps X
+    (dict(Y=FAKE2 + 4096), bd.LORA_EINVAL),                              # Y overlaps W
+    (dict(Y=FAKE3), bd.LORA_EINVAL),                                     # Y overlaps A
+    (dict(workspace=FAKE5 + 16), bd.LORA_EINVAL),                        # workspace inside Y
+])
+def test_rejected_before_launch(kw, code):
+    assert call(**kw) == code
+
+
+def test_segment_and_adapter_limits():
+    n = bd.MAX_SEGMENTS + 1
+    starts = list(range(n + 1))
+    alternating = [i % 2 - 1 for i in range(n)]               # -1, 0, -1, 0, ... never merges
+    assert call(M=n, seg_starts=starts, seg_adapter=alternating) == bd.LORA_EUNSUPPORTED
+    too_many = [FAKE3] * (bd.MAX_ADAPTERS + 1)
+    assert call(A=too_many, B=[FAKE4] * (bd.MAX_ADAPTERS + 1)) == bd.LORA_EUNSUPPORTED
+
+
+def test_empty_batch_is_a_no_op():
+    # M == 0 returns OK without touching the GPU, whatever the pointers.
+    assert call(M=0, seg_starts=[0], seg_adapter=[], X=None, Y=None) == bd.LORA_OK
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    monkeypatch.setattr(bd, "_lib", None)
+    monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "absent.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        bd.load()

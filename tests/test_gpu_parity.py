@@ -1,0 +1,255 @@
+"""Parity of the HIP path with the fp64 oracle, through the C-ABI.
+
+Bars (per call, over every element compared):
+  * bf16 output: G2 — max(|Y - Y_o| - half bf16 ulp of Y_o) <= 2e-2 rms(Y_o); G1 (the literal
+    max |Y - Y_o| <= 2e-2 rms(Y_o)) is reported and asserted where it is expected to hold;
+  * fp32 test mode: max |Y - Y_o| <= 1e-5 rms(Y_o);
+  * bf16 inputs with an fp32 store (diagnostic): max |Y - Y_o| <= 3e-5 rms(Y_o);
+  * integer-valued inputs: every partial sum is an exact integer below 2^24, so the fp32 store
+    must equal the exact result bit for bit and the bf16 store must be its correct rounding.
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gates
+from gpu_util import log, run, to_device, y_bits, y_to_numpy
+from oracle import lora_proj_ref
+from rank_adapted_gemm_amd import binding as bd
+from rank_adapted_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+F32OUT_TOL = 3e-5
+
+
+def oracle(p, rows=None, scale=None, seg_adapter=None):
+    return lora_proj_ref(p.X, p.seg_starts, p.seg_adapter if seg_adapter is None else seg_adapter,
+                         p.W, p.A, p.B, p.scale if scale is None else scale, rows=rows)
+
+
+def check_bf16(p, y_dev, ref, rows=None, literal=True):
+    y = y_to_numpy(y_dev)
+    if rows is not None:
+        y = y[rows]
+    rep = gates.report(y, ref)
+    log(f"  {p.name} bf16 rms={rep['rms']:.4g} G1={rep['g1']:.3e} G2={rep['g2']:.3e}")
+    assert rep["nonfinite"] == 0
+    assert rep["g2"] <= gates.BF16_TOL, rep
+    if literal:
+        assert rep["g1"] <= gates.BF16_TOL, rep
+    return rep
+
+
+def check_f32out(p, y_dev, ref, rows=None, tol=F32OUT_TOL):
+    y = y_to_numpy(y_dev)
+    if rows is not None:
+        y = y[rows]
+    rep = gates.report(y, ref)
+    log(f"  {p.name} f32-out rms={rep['rms']:.4g} err/rms={rep['g1']:.3e}")
+    assert rep["nonfinite"] == 0 and rep["g1"] <= tol, rep
+    return rep
+
+
+# ------------------------------------------------------------------ tiny
+def test_tiny_fp32_test_mode():
+    p = synth.tiny()
+    log(f"case tiny f32 path={bd.path(p.M, p.N, p.K, p.rank, 'f32')}")
+    y = y_to_numpy(run(p))
+    rep = gates.report(y, oracle(p))
+    log(f"  tiny f32 err/rms={rep['g1']:.3e}")
+    assert rep["nonfinite"] == 0 and rep["g1"] <= gates.F32_TOL, rep
+
+
+def test_tiny_shapes_bf16():
+    p = synth.random_problem(1, M=64, N=512, K=256, rank=16, seg_starts=[0, 32, 64], seg_adapter=[-1, 0],
+                             scale=0.5, sigma_w=1 / 16)
+    log(f"case tiny-bf16 path={bd.path(p.M, p.N, p.K, p.rank)}")
+    ref = oracle(p)
+    check_bf16(p, run(p), ref)
+    check_f32out(p, run(p, dtype="bf16_f32out"), ref)
+
+
+# ------------------------------------------------------------------ exact integer cases
+INT_CASES = {
+    # prefill path: two row tiles with a ragged tail, ragged N (2 x 256 + 8), ragged K and rank,
+    # two adapters, a mixed tile holding base rows next to adapter rows of both adapters
+    "prefill_ragged": dict(M=300, N=520, K=200, rank=48, seg_starts=[0, 5, 130, 131, 300],
+                           seg_adapter=[-1, 0, -1, 1], n_adapters=2),
+    # decode path: 64 adapter rows then six one-row base segments
+    "decode_suffix": dict(M=70, N=520, K=200, rank=48, seg_starts=[0, 64, 65, 66, 67, 68, 69, 70],
+                          seg_adapter=[0, -1, -1, -1, -1, -1, -1], n_adapters=1),
+    "single_row": dict(M=1, N=64, K=64, rank=16, seg_starts=[0, 1], seg_adapter=[0], n_adapters=1),
+    # odd N takes the element-wise store; one segment over a ragged third row tile
+    "odd_n": dict(M=513, N=257, K=72, rank=16, seg_starts=[0, 513], seg_adapter=[0], n_adapters=1),
+    "max_rank": dict(M=200, N=96, K=64, rank=512, seg_starts=[0, 100, 200], seg_adapter=[0, -1], n_adapters=1),
+}
+
+
+@pytest.mark.parametrize("name", list(INT_CASES))
+@pytest.mark.parametrize("scale", [1.0, 0.5])
+def test_integer_exact(name, scale):
+    c = INT_CASES[name]
+    p = synth.random_problem(7, scale=scale, integer=True, **c)
+    p.name = name
+    log(f"case int {name} s={scale} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    exact = oracle(p)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    yb = y_bits(run(p, dtype="bf16"))
+    assert np.array_equal(yb, gates.bf16_rne_of_f64(exact))
+
+
+# ------------------------------------------------------------------ workloads
+@pytest.fixture(scope="module")
+def layer_inputs():
+    cache = {}
+
+    def get(name, layer, K):
+        key = (name, layer, K)
+        if key not in cache:
+            w = synth.WORKLOADS[name]
+            cache[key] = synth.layer_input(w["cfg"], layer, w["M"], K)
+        return cache[key]
+    return get
+
+
+def workload(layer_inputs, name, proj, layer=0):
+    K = synth.PROJECTIONS[proj][1]
+    return synth.workload_problem(name, layer=layer, proj=proj, x=layer_inputs(name, layer, K))
+
+
+@pytest.mark.parametrize("proj", range(7))
+def test_suffix_decode_full(layer_inputs, proj):
+    """64 adapter rows + 6 base-only decode rows, every row and column checked."""
+    p = workload(layer_inputs, "suffix", proj)
+    log(f"case suffix proj={proj} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    assert bd.path(p.M, p.N, p.K, p.rank) == "decode"
+    ref = oracle(p)
+    check_bf16(p, run(p), ref)
+
+
+@pytest.mark.parametrize("proj", range(7))
+def test_mixed_batch(layer_inputs, proj):
+    """6 base-only decode rows around a 2,048-row adapter chunk (full rows for q, sampled otherwise)."""
+    p = workload(layer_inputs, "mixed", proj)
+    log(f"case mixed proj={proj} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    rows = None if proj == 0 else synth.sample_rows(p.M, p.seg_starts, 256, seed=proj)
+    ref = oracle(p, rows=rows)
+    check_bf16(p, run(p), ref, rows=rows)
+    check_f32out(p, run(p, dtype="bf16_f32out"), ref, rows=rows)
+
+
+@pytest.mark.parametrize("proj", range(7))
+def test_prefill16k_sampled(layer_inputs, proj):
+    """The 16,384-row adapted prefill at full size, in the launch configuration the benchmark times."""
+    p = workload(layer_inputs, "prefill16k", proj)
+    log(f"case prefill16k proj={proj} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    assert bd.path(p.M, p.N, p.K, p.rank) == "prefill"
+    rows = synth.sample_rows(p.M, p.seg_starts, 256, seed=100 + proj)
+    ref = oracle(p, rows=rows)
+    check_bf16(p, run(p), ref, rows=rows, literal=False)
+
+
+@pytest.mark.parametrize("proj", [0, 4, 6])
+def test_stack32k_layer_sampled(layer_inputs, proj):
+    p = workload(layer_inputs, "stack32k", proj)
+    log(f"case stack32k proj={proj}")
+    rows = synth.sample_rows(p.M, p.seg_starts, 192, seed=200 + proj)
+    ref = oracle(p, rows=rows)
+    check_bf16(p, run(p), ref, rows=rows, literal=False)
+
+
+# ------------------------------------------------------------------ invariants
+@pytest.mark.parametrize("name", ["mixed", "suffix"])
+def test_base_rows_bitwise_unchanged_by_adapter(layer_inputs, name):
+    """Rows of base-only requests come out identical whether or not other rows use the adapter."""
+    p = workload(layer_inputs, name, 0)
+    log(f"case base-row invariance {name}")
+    dev = to_device(p)
+    y_mixed = y_bits(run(p, dev_inputs=dev))
+    y_plain = y_bits(run(p, dev_inputs=dev, seg_adapter=[-1] * len(p.seg_adapter)))
+    base = np.concatenate([np.arange(p.seg_starts[g], p.seg_starts[g + 1])
+                           for g in range(len(p.seg_adapter)) if p.seg_adapter[g] < 0])
+    a = synth.bf16_bits_to_f32(y_mixed[base])
+    b = synth.bf16_bits_to_f32(y_plain[base])
+    assert np.array_equal(a, b)          # +0 and -0 compare equal
+    adapter_rows = np.setdiff1d(np.arange(p.M), base)
+    assert not np.array_equal(y_mixed[adapter_rows], y_plain[adapter_rows])
+
+
+def test_bitwise_deterministic(layer_inputs):
+    p = workload(layer_inputs, "mixed", 6)
+    log("case determinism mixed/down")
+    dev = to_device(p)
+    first = y_bits(run(p, dev_inputs=dev))
+    for _ in range(2):
+        assert np.array_equal(first, y_bits(run(p, dev_inputs=dev)))
+
+
+# ------------------------------------------------------------------ edge cases
+def test_edge_tables():
+    base = dict(M=1000, N=264, K=128, rank=32, n_adapters=3)
+    g = np.random.Generator(np.random.PCG64(5))
+    cuts = np.sort(g.choice(np.arange(1, 1000), 199, replace=False))
+    starts = np.concatenate([[0], cuts, [1000]])
+    adapters = g.integers(-1, 3, size=200)
+    cases = {
+        "many_segments": (starts, adapters),
+        "empty_segments": ([0, 0, 10, 10, 500, 1000, 1000], [1, 0, 2, -1, 0, 2]),
+        "same_adapter_neighbours": ([0, 100, 200, 300, 1000], [0, 0, 0, -1]),
+        "all_base": ([0, 1000], [-1]),
+    }
+    for name, (s, a) in cases.items():
+        p = synth.random_problem(9, seg_starts=s, seg_adapter=a, **base)
+        p.name = name
+        log(f"case edge {name}")
+        check_bf16(p, run(p), oracle(p))
+
+
+def test_edge_shapes():
+    for M, N, K, r in ((1, 5120, 5120, 256), (2, 8, 8, 16), (129, 72, 64, 16), (128, 200, 136, 32),
+                       (257, 1000, 520, 256)):
+        s = [0, M // 2, M] if M > 1 else [0, 1]
+        a = [-1, 0] if M > 1 else [0]
+        p = synth.random_problem(21, M=M, N=N, K=K, rank=r, seg_starts=s, seg_adapter=a)
+        p.name = f"shape M={M} N={N} K={K} r={r}"
+        log(f"case {p.name} path={bd.path(M, N, K, r)}")
+        check_bf16(p, run(p), oracle(p))
+
+
+def test_scale_zero_equals_base():
+    p = synth.random_problem(3, M=300, N=256, K=256, rank=32, seg_starts=[0, 300], seg_adapter=[0], scale=0.0)
+    dev = to_device(p)
+    a = synth.bf16_bits_to_f32(y_bits(run(p, dev_inputs=dev)))
+    b = synth.bf16_bits_to_f32(y_bits(run(p, dev_inputs=dev, seg_adapter=[-1])))
+    assert np.array_equal(a, b)
+
+
+def test_empty_batch():
+    import torch
+    X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
+    W = torch.zeros((32, 64), dtype=torch.bfloat16, device="cuda")
+    y = bd.lora_proj(X, [0], [], W, [], [], 1.0)
+    assert tuple(y.shape) == (0, 32)
+
+
+# ------------------------------------------------------------------ negative controls
+@pytest.mark.parametrize("arm", ["adapter_off", "scale_doubled", "base_rows_given_adapter", "boundary_off_by_one"])
+def test_negative_control_fails_gate(arm):
+    """Deliberately wrong calls of the right kernels must fail the bf16 gate against the oracle."""
+    p = synth.random_problem(17, M=300, N=520, K=256, rank=32, seg_starts=[0, 40, 300], seg_adapter=[-1, 0])
+    ref = oracle(p)
+    if arm == "adapter_off":
+        y = run(p, seg_adapter=[-1, -1])
+    elif arm == "scale_doubled":
+        y = run(p, scale=2 * p.scale)
+    elif arm == "base_rows_given_adapter":
+        y = run(p, seg_adapter=[0, 0])
+    else:
+        q = synth.random_problem(17, M=300, N=520, K=256, rank=32, seg_starts=[0, 41, 300], seg_adapter=[-1, 0])
+        y = run(q)
+    assert not gates.passes_bf16(y_to_numpy(y), ref), arm
