@@ -168,7 +168,11 @@ def time_steps(runner, steps, warmup, hip):
 
 # ------------------------------------------------------------------ CPU baseline
 def cpu_baseline(rows: int):
-    """fp64 oracle on `rows` token rows of each prefill16k projection (host recipe weights)."""
+    """fp64 oracle on `rows` token rows of each prefill16k projection (host recipe weights).
+
+    The default, 16384 rows, is the whole workload; smaller values time a row sample
+    (rows are independent, so the rate does not depend on which rows).
+    """
     from oracle import lora_proj_ref
     try:
         import threadpoolctl
@@ -204,32 +208,10 @@ def traffic_record():
     return None
 
 
-# ------------------------------------------------------------------ main
-def main(argv=None):
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--decode-steps", type=int, default=20)
-    ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=4096)
-    a = ap.parse_args(argv)
-    if a.gpus != 1:
-        print(f"bench.py runs on one GPU only: the projection is measured at one GPU's share "
-              f"(requested --gpus {a.gpus}); rows shard across GPUs without any exchange.", file=sys.stderr)
-        return 2
-    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py is single-process; do not launch it with several ranks", file=sys.stderr)
-        return 2
 
+# ------------------------------------------------------------------ the two timed workloads
+def run_prefill(a, dev, hip):
     import torch
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    bd.load()
-    hip = HipEvents()
-
-    # ---------------- prefill16k
     w = synth.WORKLOADS["prefill16k"]
     log("prefill16k: drawing inputs on the device")
     layer = device_layer(w["cfg"], 0, w["M"], dev)
@@ -244,34 +226,77 @@ def main(argv=None):
     per_proj_ms = main_ms.mean(axis=0)
     log(f"prefill16k: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s; "
         + ", ".join(f"{p['name']} {t:.3f}" for p, t in zip(runner.calls, per_proj_ms)))
-    traffic = traffic_record()
     roofline = dict(bound="mfma", achieved=round(main_achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
-                    frac=round(main_achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic,
-                    kernel="main_kernel<Tile<256,256,2,2>, bf16 out>",
+                    frac=round(main_achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic_record(),
+                    kernel="main_kernel<Tile<256,256,2,4>, bf16 out>",
                     launch_avg_ms=round(float(main_ms.mean()), 4),
                     per_projection_ms={p["name"]: round(float(t), 4) for p, t in zip(runner.calls, per_proj_ms)})
     del runner, layer
     torch.cuda.empty_cache()
+    return dict(value=value, ms_per_step=ms_per_step, flops=step_flops, bytes=byts, roofline=roofline)
 
-    # ---------------- suffix decode stack
-    decode = None
-    if not a.no_decode:
-        w5 = synth.WORKLOADS["suffix"]
-        log("suffix: drawing 24 layers on the device")
-        layers = [device_layer(w5["cfg"], l, w5["M"], dev) for l in range(w5["layers"])]
-        runner = StepRunner(layers, w5["seg_starts"], w5["seg_adapter"], w5["scale"], dev)
-        dmain, dshrink, dbytes = runner.work()
-        wall5, main5 = time_steps(runner, a.decode_steps, a.warmup, hip)
-        ms5 = wall5 * 1e3 / a.decode_steps
-        gbs = dbytes / (ms5 / 1e3) / 1e9
-        decode = dict(workload="suffix: 24 layers x 7 projections, 64 adapter rows + 6 base-only decode rows, r=256",
-                      value=round(gbs, 1), unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
-                      ms_per_step=round(ms5, 4), bytes_per_step=dbytes, steps=a.decode_steps,
-                      tflops=round((dmain + dshrink) / (ms5 / 1e3) / 1e12, 2),
-                      output_kernel_avg_ms=round(float(main5.mean()), 5))
-        log(f"suffix: {ms5:.3f} ms/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
-        del runner, layers
-        torch.cuda.empty_cache()
+
+def run_decode(a, dev, hip):
+    import torch
+    w5 = synth.WORKLOADS["suffix"]
+    log("suffix: drawing 24 layers on the device")
+    layers = [device_layer(w5["cfg"], l, w5["M"], dev) for l in range(w5["layers"])]
+    runner = StepRunner(layers, w5["seg_starts"], w5["seg_adapter"], w5["scale"], dev)
+    dmain, dshrink, dbytes = runner.work()
+    wall5, main5 = time_steps(runner, a.decode_steps, a.warmup, hip)
+    ms5 = wall5 * 1e3 / a.decode_steps
+    gbs = dbytes / (ms5 / 1e3) / 1e9
+    log(f"suffix: {ms5:.3f} ms/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    del runner, layers
+    torch.cuda.empty_cache()
+    return dict(workload="suffix: 24 layers x 7 projections, 64 adapter rows + 6 base-only decode rows, r=256",
+                value=round(gbs, 1), unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
+                ms_per_step=round(ms5, 4), bytes_per_step=dbytes, steps=a.decode_steps,
+                tflops=round((dmain + dshrink) / (ms5 / 1e3) / 1e12, 2),
+                output_kernel_avg_ms=round(float(main5.mean()), 5))
+
+
+# ------------------------------------------------------------------ main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=20)
+    ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+                    help="time one workload only (for profiler runs)")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="run a plain device copy of MIB mebibytes (reads MIB, writes MIB) five times and exit; "
+                         "calibrates the FETCH_SIZE / WRITE_SIZE counters")
+    a = ap.parse_args(argv)
+    if a.gpus != 1:
+        print(f"bench.py runs on one GPU only: the projection is measured at one GPU's share "
+              f"(requested --gpus {a.gpus}); rows shard across GPUs without any exchange.", file=sys.stderr)
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py is single-process; do not launch it with several ranks", file=sys.stderr)
+        return 2
+
+    import torch
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    if a.copy_probe:
+        n = a.copy_probe * (1 << 20) // 4
+        src = torch.ones(n, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 x {a.copy_probe} MiB read + {a.copy_probe} MiB written")
+        return 0
+    bd.load()
+    hip = HipEvents()
+    w = synth.WORKLOADS["prefill16k"]
+    pre = run_prefill(a, dev, hip) if a.only in ("all", "prefill") else {}
+    decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
     hip.close()
 
     cpu = None
@@ -279,15 +304,17 @@ def main(argv=None):
         log("cpu baseline: fp64 oracle on sampled rows")
         cpu = cpu_baseline(a.cpu_rows)
 
-    out = dict(metric=METRIC, value=round(value, 2), unit="TFLOP/s", n_gpus=1, steps=a.steps, warmup=a.warmup,
-               ms_per_step=round(ms_per_step, 4), higher_is_better=True, scaling="weak", vs_baseline=None,
+    value, ms_per_step = pre.get("value"), pre.get("ms_per_step")
+    out = dict(metric=METRIC, value=None if value is None else round(value, 2), unit="TFLOP/s", n_gpus=1,
+               steps=a.steps, warmup=a.warmup, ms_per_step=None if ms_per_step is None else round(ms_per_step, 4),
+               higher_is_better=True, scaling="weak", vs_baseline=None,
                dtype="bf16", data="synthetic",
                config=dict(workload="prefill16k: one adapted layer, 16384 rows all naming the adapter, "
                                     "7 projections (q,k,v,o 5120->5120; gate,up 5120->17408; down 17408->5120), "
                                     "rank 256, s=1",
-                           M=w["M"], rank=synth.RANK, flop_per_step=step_flops, bytes_per_step=byts,
+                           M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
-               roofline=roofline, cpu_baseline=cpu, decode=decode)
+               roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -11,10 +11,11 @@
 //           rows, acc += T_hi B_a^T + T_lo B_a^T over the rank (rows of other
 //           segments read as zero), then one round-to-nearest-even store.
 //
-// Both run the same LDS-staged MFMA K-loop: 16-byte buffer loads of 64-element
-// K slabs into registers, a double-buffered LDS stage with an XOR swizzle on
-// 16-byte chunks (conflict-free ds_read_b128), and v_mfma_f32_32x32x16_bf16
-// with fp32 accumulators.  The MFMA "A" operand is the weight side (rows n) and
+// Both run the same LDS-staged MFMA K-loop: 32-element K slabs move from
+// global memory straight into a ring of four LDS stages (buffer_load ... lds,
+// 16 bytes per lane, three stages in flight), an XOR swizzle on 16-byte chunks
+// keeps ds_read_b128 conflict-free, and v_mfma_f32_32x32x16_bf16 accumulates in
+// fp32.  The MFMA "A" operand is the weight side (rows n) and
 // "B" is the activation side (rows m), so each lane ends with four consecutive
 // output columns of one row and stores them as one 8-byte write.
 //
@@ -31,19 +32,29 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-constexpr int BK = 64;          // K elements per LDS stage (128 bytes per tile row)
+constexpr int BK = 32;          // K elements per LDS stage (64 bytes per tile row)
 constexpr int ROW_BYTES = BK * 2;
+constexpr int NSTAGE = 4;       // LDS ring depth; NSTAGE - 1 stages are in flight
+
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
   // word3 0x00020000: raw 32-bit data, no swizzle (gfx9 family)
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
 }
 
+// The same descriptor as four words, for the inline-assembly loads.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xFFFFu), int32_t(bytes), 0x00020000};
+}
+
 // One operand of a K-loop: rows of a row-major bf16 matrix whose reduction
-// index is contiguous.  Tile row i is global row row0 + i; rows outside
-// [lo, hi) read as zero.
+// index is contiguous.  Tile row i is global row row0 + i.  Rows past the
+// operand's extent are never fetched; rows outside [lo, hi) are zeroed in the
+// MFMA operands when the loop masks rows.
 struct Side {
-  __amdgpu_buffer_rsrc_t res;
+  i32x4 res;
   uint32_t ld_bytes;
   int32_t row0, lo, hi;
 };
@@ -53,41 +64,62 @@ struct Side {
 template <int TN_, int TM_, int WN_, int WM_>
 struct Tile {
   static constexpr int TN = TN_, TM = TM_, WN = WN_, WM = WM_;
-  static constexpr int NT = 64 * WN * WM;
+  static constexpr int NW = WN * WM;
+  static constexpr int NT = 64 * NW;
   static constexpr int FN = TN / WN / 32;        // MFMA tiles per wave along n
   static constexpr int FM = TM / WM / 32;        // ... along m
-  static constexpr int CN = TN * 8 / NT;         // 16-byte chunks per thread per stage, weight side
-  static constexpr int CM = TM * 8 / NT;         // ... activation side
   static constexpr int STAGE = (TN + TM) * ROW_BYTES;
+  static constexpr int GROUPS = STAGE / 1024;    // 16-row groups: one wave-wide 16-byte load each
+  static constexpr int PW = GROUPS / NW;         // loads per wave per stage
   static_assert(FN >= 1 && FM >= 1, "wave tile smaller than one MFMA tile");
-  static_assert(TN * 8 % NT == 0 && TM * 8 % NT == 0, "tile rows must split evenly over threads");
+  static_assert(TN % 16 == 0 && TM % 16 == 0 && GROUPS % NW == 0, "row groups must split evenly over waves");
 };
 
-// ------------------------------------------------------------------ staging
-template <int ROWS, int NT>
-__device__ __forceinline__ void load_rows(u32x4 (&v)[ROWS * 8 / NT], const Side& s, int k0, int kdim, int tid) {
-#pragma unroll
-  for (int i = 0; i < ROWS * 8 / NT; ++i) {
-    const int q = tid + i * NT;
-    const int r = q >> 3, c = q & 7;
-    const int grow = s.row0 + r;
-    const int kk = k0 + c * 8;
-    const bool ok = grow >= s.lo && grow < s.hi && kk < kdim;
-    const uint32_t off = ok ? uint32_t(grow) * s.ld_bytes + uint32_t(kk) * 2u : kMaskedOffset;
-    v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(s.res, off, 0, 0));
-  }
+// Chunk c (16 bytes) of tile row r lives at slot c ^ ((r >> 2) & 3).  The LDS
+// has 64 four-byte banks and serves 16 lanes of a ds_read_b128 per cycle;
+// those lanes read one chunk of 16 consecutive rows.  A 64-byte row covers a
+// quarter of the banks, and the XOR gives the four rows that share a quarter
+// four distinct slots, so no two lanes of a cycle share a bank.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ ((r >> 2) & 3)) << 4); }
+
+// Global -> LDS: one buffer_load_dwordx4 with the lds flag writes 64 lanes x
+// 16 bytes contiguously at M0, i.e. 16 tile rows; lane l fills row l/4, slot
+// l%4 and so fetches the chunk that the swizzle puts there.  Issued from
+// inline assembly (M0 is set in the same statement), so completion is tracked
+// by the explicit vmcnt waits of the K-loop.
+__device__ __forceinline__ void dma16(const i32x4& res, uint32_t voff, uint32_t lds_addr) {
+  const i32x4 r{__builtin_amdgcn_readfirstlane(res[0]), __builtin_amdgcn_readfirstlane(res[1]),
+                __builtin_amdgcn_readfirstlane(res[2]), __builtin_amdgcn_readfirstlane(res[3])};
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
-// Chunk c of tile row r lives at slot c ^ (r & 7): eight consecutive rows read
-// at one chunk index land on eight distinct 16-byte slots.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ (r & 7)) << 4); }
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 
-template <int ROWS, int NT>
-__device__ __forceinline__ void store_rows(char* base, const u32x4 (&v)[ROWS * 8 / NT], int tid) {
+// Wait until at most `stages` later stages of PW loads each are still in flight.
+template <int PW>
+__device__ __forceinline__ void wait_stages(int stages) {
+  static_assert(PW * (NSTAGE - 2) <= 63, "vmcnt holds at most 63");
+  if (stages >= 3 && NSTAGE > 4) wait_vm<PW * (NSTAGE > 4 ? 3 : 0)>();
+  else if (stages >= 2) wait_vm<2 * PW>();
+  else if (stages == 1) wait_vm<PW>();
+  else wait_vm<0>();
+}
+
+template <class C>
+__device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane) {
+  // LDS byte offset of the stage (M0 takes LDS addresses, not flat ones)
+  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)stage));
 #pragma unroll
-  for (int i = 0; i < ROWS * 8 / NT; ++i) {
-    const int q = tid + i * NT;
-    *reinterpret_cast<u32x4*>(base + lds_off(q >> 3, q & 7)) = v[i];
+  for (int i = 0; i < C::PW; ++i) {
+    const int g = wave * C::PW + i;                 // 16-row group of the stage (uniform)
+    const bool wside = g * 16 < C::TN;
+    const Side& sd = wside ? ws : xs;
+    const int r = g * 16 + (lane >> 2) - (wside ? 0 : C::TN);
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const uint32_t off = uint32_t(sd.row0 + r) * sd.ld_bytes + uint32_t(k0 + c * 8) * 2u;
+    dma16(sd.res, off, base + uint32_t(g) * 1024u);
   }
 }
 
@@ -95,10 +127,12 @@ __device__ __forceinline__ bf16x8 read_frag(const char* base, int r, int c) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lds_off(r, c)));
 }
 
-// acc += (weight tile) x (activation tile)^T over one 64-wide stage.
-template <class C>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[C::FN][C::FM], const char* wt, const char* xt,
-                                          int wrow, int xrow, int lane) {
+// acc += (weight tile) x (activation tile)^T over one 32-wide stage (two k16
+// substeps).  MASK_ROWS zeroes activation rows outside [lo, hi); TAIL zeroes
+// the chunks at or past kdim on both sides.
+template <class C, bool MASK_ROWS, bool TAIL>
+__device__ __forceinline__ void mma_stage(f32x16 (&acc)[C::FN][C::FM], const char* wt, const char* xt, int wrow,
+                                          int xrow, int lane, int xg0, int lo, int hi, int k0, int kdim) {
 #pragma unroll
   for (int s = 0; s < BK / 16; ++s) {
     const int c = 2 * s + (lane >> 5);
@@ -107,6 +141,21 @@ __device__ __forceinline__ void mma_stage(f32x16 (&acc)[C::FN][C::FM], const cha
     for (int i = 0; i < C::FN; ++i) a[i] = read_frag(wt, wrow + i * 32 + (lane & 31), c);
 #pragma unroll
     for (int j = 0; j < C::FM; ++j) b[j] = read_frag(xt, xrow + j * 32 + (lane & 31), c);
+    if constexpr (TAIL) {
+      if (k0 + c * 8 >= kdim) {
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) a[i] = bf16x8{};
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) b[j] = bf16x8{};
+      }
+    }
+    if constexpr (MASK_ROWS) {
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) {
+        const int grow = xg0 + xrow + j * 32 + (lane & 31);
+        if (grow < lo || grow >= hi) b[j] = bf16x8{};
+      }
+    }
 #pragma unroll
     for (int i = 0; i < C::FN; ++i)
 #pragma unroll
@@ -115,43 +164,141 @@ __device__ __forceinline__ void mma_stage(f32x16 (&acc)[C::FN][C::FM], const cha
   }
 }
 
-// Double-buffered K-loop over `ntiles` stages.  src(t, ws, xs, k0) names the
-// weight-side and activation-side operands and the K offset of stage t.
-template <class C, class Src>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src,
-                                       char* smem, int tid, int wn, int wm) {
-  if (ntiles <= 0) return;
-  const int lane = tid & 63;
-  const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
-  u32x4 wv[C::CN], xv[C::CM];
-  {
-    Side ws, xs;
-    int k0;
-    src(0, ws, xs, k0);
-    load_rows<C::TN, C::NT>(wv, ws, k0, kdim, tid);
-    load_rows<C::TM, C::NT>(xv, xs, k0, kdim, tid);
-    store_rows<C::TN, C::NT>(smem, wv, tid);
-    store_rows<C::TM, C::NT>(smem + C::TN * ROW_BYTES, xv, tid);
-  }
-  __syncthreads();
-  for (int t = 0; t < ntiles; ++t) {
-    char* cur = smem + (t & 1) * C::STAGE;
-    const bool more = t + 1 < ntiles;
-    if (more) {
+// K-loop over `ntiles` stages.  src(t, ws, xs, k0) names the weight-side and
+// activation-side operands and the K offset of stage t; stages from `ntail` on
+// reach past kdim and have their out-of-range chunks zeroed.  Stage t lives in
+// ring slot t % NSTAGE; the loads of stages t+1 .. t+NSTAGE-2 stay in flight
+// while stage t is consumed.  With MASK_ROWS the activation rows outside the
+// activation side's [lo, hi) enter the MFMAs as zero.
+template <class C, bool MASK_ROWS, bool TAIL, class Src>
+__device__ __forceinline__ void k_stages(f32x16 (&acc)[C::FN][C::FM], int t0, int t1, int ntiles, int kdim, Src& src,
+                                         char* smem, int wave, int lane, int wrow, int xrow) {
+  for (int t = t0; t < t1; ++t) {
+    // stage t has landed once at most the loads of the stages issued after it remain
+    wait_stages<C::PW>(min(NSTAGE - 2, ntiles - 1 - t));
+    __syncthreads();
+    if (t + NSTAGE - 1 < ntiles) {   // refill the slot every wave finished reading in stage t-1
       Side ws, xs;
       int k0;
-      src(t + 1, ws, xs, k0);
-      load_rows<C::TN, C::NT>(wv, ws, k0, kdim, tid);
-      load_rows<C::TM, C::NT>(xv, xs, k0, kdim, tid);
+      src(t + NSTAGE - 1, ws, xs, k0);
+      issue_stage<C>(smem + ((t + NSTAGE - 1) % NSTAGE) * C::STAGE, ws, xs, k0, wave, lane);
     }
-    mma_stage<C>(acc, cur, cur + C::TN * ROW_BYTES, wrow, xrow, lane);
-    if (more) {
-      char* nxt = smem + ((t + 1) & 1) * C::STAGE;
-      store_rows<C::TN, C::NT>(nxt, wv, tid);
-      store_rows<C::TM, C::NT>(nxt + C::TN * ROW_BYTES, xv, tid);
+    Side ws, xs;
+    int k0;
+    src(t, ws, xs, k0);
+    const char* cur = smem + (t % NSTAGE) * C::STAGE;
+    mma_stage<C, MASK_ROWS, TAIL>(acc, cur, cur + C::TN * ROW_BYTES, wrow, xrow, lane, xs.row0, xs.lo, xs.hi, k0,
+                                  kdim);
+  }
+}
+
+template <class C, bool MASK_ROWS, class Src>
+__device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, int ntail, int kdim, Src src,
+                                       char* smem, int tid, int wn, int wm) {
+  if (ntiles <= 0) return;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
+#pragma unroll
+  for (int p = 0; p < NSTAGE - 1; ++p) {
+    if (p < ntiles) {
+      Side ws, xs;
+      int k0;
+      src(p, ws, xs, k0);
+      issue_stage<C>(smem + p * C::STAGE, ws, xs, k0, wave, lane);
     }
+  }
+  k_stages<C, MASK_ROWS, false>(acc, 0, ntail, ntiles, kdim, src, smem, wave, lane, wrow, xrow);
+  k_stages<C, MASK_ROWS, true>(acc, ntail, ntiles, ntiles, kdim, src, smem, wave, lane, wrow, xrow);
+  __syncthreads();   // the ring is reused by whatever runs next
+}
+
+// Ping-pong K-loop for 8-wave tiles.  The two waves on each SIMD belong to
+// different groups (waves 0-3 and 4-7), and the groups run one barrier
+// interval apart:
+//
+//   group 0:  M(0) | C(0) | M(1) | C(1) | ... | C(T-1) | -
+//   group 1:   -   | M(0) | C(0) | M(1) | ... | M(T-1) | C(T-1)
+//
+// so in every interval one wave per SIMD issues nothing but MFMAs on
+// fragments already in registers (C) while the other does the memory work (M):
+// it refills the LDS ring with stage t+D, reads every fragment of stage t into
+// registers (zeroing masked rows and the K tail there, off the MFMA path), and
+// confirms its own loads of stage t+1.  A stage is therefore complete and
+// visible one barrier before either group reads it, and a ring slot is refilled
+// only after both groups have read it.
+template <class C, bool MASK_ROWS, class Src>
+__device__ __forceinline__ void k_loop_pingpong(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src,
+                                                char* smem, int tid, int wn, int wm) {
+  static_assert(C::NW == 8, "ping-pong needs two waves per SIMD");
+  constexpr int D = NSTAGE - 1;
+  if (ntiles <= 0) return;
+  const int lane = tid & 63, wave = tid >> 6;
+  const bool trailing = wave >= 4;
+  const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
+#pragma unroll
+  for (int p = 0; p < D; ++p) {
+    if (p < ntiles) {
+      Side ws, xs;
+      int k0;
+      src(p, ws, xs, k0);
+      issue_stage<C>(smem + p * C::STAGE, ws, xs, k0, wave, lane);
+    }
+  }
+  wait_stages<C::PW>(min(D, ntiles) - 1);   // stage 0 complete
+  __syncthreads();
+  if (trailing) __syncthreads();
+  bf16x8 fa[BK / 16][C::FN], fb[BK / 16][C::FM];
+  for (int t = 0; t < ntiles; ++t) {
+    // ---- M(t)
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + D < ntiles) {
+      Side ws, xs;
+      int k0;
+      src(t + D, ws, xs, k0);
+      issue_stage<C>(smem + ((t + D) % NSTAGE) * C::STAGE, ws, xs, k0, wave, lane);
+    }
+    Side ws, xs;
+    int k0;
+    src(t, ws, xs, k0);
+    const char* wt = smem + (t % NSTAGE) * C::STAGE;
+    const char* xt = wt + C::TN * ROW_BYTES;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int c = 2 * s + (lane >> 5);
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) fa[s][i] = read_frag(wt, wrow + i * 32 + (lane & 31), c);
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) fb[s][j] = read_frag(xt, xrow + j * 32 + (lane & 31), c);
+      if (k0 + BK > kdim && k0 + c * 8 >= kdim) {   // the first test is uniform: only tail stages pay
+#pragma unroll
+        for (int i = 0; i < C::FN; ++i) fa[s][i] = bf16x8{};
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) fb[s][j] = bf16x8{};
+      }
+      if constexpr (MASK_ROWS) {
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) {
+          const int grow = xs.row0 + xrow + j * 32 + (lane & 31);
+          if (grow < xs.lo || grow >= xs.hi) fb[s][j] = bf16x8{};
+        }
+      }
+    }
+    // own loads of stage t+1 complete; loads of later stages may stay in flight
+    wait_stages<C::PW>(min(t + D, ntiles - 1) - (t + 1));
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+    // ---- C(t)
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s)
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
+  if (!trailing) __syncthreads();
 }
 
 // ------------------------------------------------------------------ scheduling
@@ -193,14 +340,14 @@ __device__ __forceinline__ uint32_t pack2(float a, float b) { return bf16_bits(a
 // T = s acc stored as bf16 hi and lo parts on the segment's rows only.
 template <class C>
 __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, AdapterTable at, int ntn, int ntm) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
   int tn, tm;
   tile_of_block(blockIdx.x, ntn, ntm, tn, tm);
   const int j0 = tn * C::TN, m0 = tm * C::TM;
   const int m1 = min(m0 + C::TM, p.M);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
-  const auto xres = make_rsrc(p.X, p.x_bytes);
+  const i32x4 xres = make_rsrc_words(p.X, p.x_bytes);
   const auto tres = make_rsrc(p.T, p.t_bytes);
   const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.rank) * 2u;   // T_lo follows T_hi
 
@@ -208,7 +355,8 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
     const int a = st.adapter[g];
     if (a < 0) continue;
     const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
-    const Side as{make_rsrc(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.rank};
+    // rows of the tile outside [lo, hi) are computed but never stored
+    const Side as{make_rsrc_words(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.rank};
     const Side xs{xres, uint32_t(p.K) * 2u, m0, lo, hi};
     f32x16 acc[C::FN][C::FM];
 #pragma unroll
@@ -216,7 +364,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
 #pragma unroll
       for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
     const int nk = (p.K + BK - 1) / BK;
-    k_loop<C>(acc, nk, p.K,
+    k_loop<C, false>(acc, nk, p.K / BK, p.K,
               [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = t * BK; },
               smem, tid, wn, wm);
     // acc[i][j][r]: rank index j0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
@@ -255,7 +403,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
 template <class C, bool F32_OUT>
 __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, AdapterTable at, int has_adapter,
                                                      int ntn, int ntm) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
   int tn, tm;
   tile_of_block(blockIdx.x, ntn, ntm, tn, tm);
   const int n0 = tn * C::TN, m0 = tm * C::TM;
@@ -271,79 +419,94 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
 
   // base product over K
   {
-    const Side ws{make_rsrc(p.W, p.w_bytes), uint32_t(p.K) * 2u, n0, 0, p.N};
-    const Side xs{make_rsrc(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0, 0, p.M};
+    const Side ws{make_rsrc_words(p.W, p.w_bytes), uint32_t(p.K) * 2u, n0, 0, p.N};
+    const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0, 0, p.M};
     const int nk = (p.K + BK - 1) / BK;
-    k_loop<C>(acc, nk, p.K, [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BK; },
-              smem, tid, wn, wm);
+    auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BK; };
+    if constexpr (C::NW == 8) k_loop_pingpong<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
+    else k_loop<C, false>(acc, nk, p.K / BK, p.K, src, smem, tid, wn, wm);
   }
 
   // expand: for each adapter segment overlapping the tile, stages alternate
-  // T_hi and T_lo against the same 64-wide slab of B_a
+  // T_hi and T_lo against the same 32-wide slab of B_a
   if (has_adapter) {
-    const auto tres = make_rsrc(p.T, p.t_bytes);
+    const i32x4 tres = make_rsrc_words(p.T, p.t_bytes);
     const uint32_t ld = uint32_t(p.rank) * 2u;
     const int lo_row0 = m0 + p.M;          // T_lo rows sit M rows after T_hi rows
     for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
       const int a = st.adapter[g];
       if (a < 0) continue;
       const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
-      const Side bs{make_rsrc(at.B[a], p.b_bytes), ld, n0, 0, p.N};
+      const Side bs{make_rsrc_words(at.B[a], p.b_bytes), ld, n0, 0, p.N};
       const Side th{tres, ld, m0, lo, hi};
       const Side tl{tres, ld, lo_row0, lo + p.M, hi + p.M};
       const int nr = 2 * ((p.rank + BK - 1) / BK);
-      k_loop<C>(acc, nr, p.rank,
-                [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; },
-                smem, tid, wn, wm);
+      auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
+      if constexpr (C::NW == 8) k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm);
+      else k_loop<C, true>(acc, nr, 2 * (p.rank / BK), p.rank, src, smem, tid, wn, wm);
     }
   }
 
   // epilogue: acc[i][j][r] is column n0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4
-  // of row m0 + wm*(TM/WM) + j*32 + lane%32
+  // of row m0 + wm*(TM/WM) + j*32 + lane%32.  When N % 4 == 0 each lane writes its
+  // four consecutive columns at once; otherwise one element at a time.
   const auto yres = make_rsrc(p.Y, p.y_bytes);
-  const bool vec = (p.N & 3) == 0;
+  const int mrow = m0 + wm * (C::TM / C::WM) + (lane & 31);
+  const int ncol = n0 + wn * (C::TN / C::WN) + (lane >> 5) * 4;
+  if ((p.N & 3) == 0) {
 #pragma unroll
-  for (int j = 0; j < C::FM; ++j) {
-    const int m = m0 + wm * (C::TM / C::WM) + j * 32 + (lane & 31);
-    const bool row_ok = m < p.M;
+    for (int j = 0; j < C::FM; ++j) {
+      const int m = mrow + j * 32;
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i)
+      for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int n = n0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
-        const float v[4] = {acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1], acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3]};
-        const uint32_t e0 = uint32_t(m) * uint32_t(p.N) + uint32_t(n);
-        if (vec) {
-          const bool ok = row_ok && n < p.N;
+        for (int q = 0; q < 4; ++q) {
+          const int n = ncol + i * 32 + q * 8;
+          const bool ok = m < p.M && n < p.N;
+          const uint32_t e0 = uint32_t(m) * uint32_t(p.N) + uint32_t(n);
           if constexpr (F32_OUT) {
-            const u32x4 w{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
-                          __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
+            // element values go through __float_as_uint: a bit cast applied to a vector-element
+            // lvalue would read element 0
+            const u32x4 w{__float_as_uint(acc[i][j][q * 4 + 0]), __float_as_uint(acc[i][j][q * 4 + 1]),
+                          __float_as_uint(acc[i][j][q * 4 + 2]), __float_as_uint(acc[i][j][q * 4 + 3])};
             __builtin_amdgcn_raw_buffer_store_b128(w, yres, ok ? e0 * 4u : kMaskedOffset, 0, 0);
           } else {
-            const u32x2 w{pack2(v[0], v[1]), pack2(v[2], v[3])};
+            const u32x2 w{pack2(acc[i][j][q * 4 + 0], acc[i][j][q * 4 + 1]), pack2(acc[i][j][q * 4 + 2], acc[i][j][q * 4 + 3])};
             __builtin_amdgcn_raw_buffer_store_b64(w, yres, ok ? e0 * 2u : kMaskedOffset, 0, 0);
           }
-        } else {
+        }
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) {
+      const int m = mrow + j * 32;
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
-            const bool ok = row_ok && n + e < p.N;
+            const int n = ncol + i * 32 + q * 8 + e;
+            const bool ok = m < p.M && n < p.N;
+            const uint32_t e0 = uint32_t(m) * uint32_t(p.N) + uint32_t(n);
             if constexpr (F32_OUT) {
-              __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v[e]), yres,
-                                                    ok ? (e0 + e) * 4u : kMaskedOffset, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[i][j][q * 4 + e]), yres,
+                                                    ok ? e0 * 4u : kMaskedOffset, 0, 0);
             } else {
-              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(bf16_bits(v[e])), yres,
-                                                    ok ? (e0 + e) * 2u : kMaskedOffset, 0, 0);
+              __builtin_amdgcn_raw_buffer_store_b16(uint16_t(bf16_bits(acc[i][j][q * 4 + e])), yres,
+                                                    ok ? e0 * 2u : kMaskedOffset, 0, 0);
             }
           }
-        }
-      }
+    }
   }
 }
 
-// Tile choices.  Large M: 256x256 tiles, four waves of 128x128 (one wave per
-// SIMD, 256 fp32 accumulators per lane, 128 KiB of LDS).  Small M (decode
-// batches) and the shrink: smaller tiles so enough blocks exist to fill the CUs.
-using MainBig = Tile<256, 256, 2, 2>;
+// Tile choices.  Large M: 256x256 tiles, eight waves of 128 (n) x 64 (m): two
+// waves per SIMD, so one wave's MFMAs cover the other's LDS waits and
+// barriers; 128 fp32 accumulators per lane, 128 KiB of LDS for the ring.
+// Small M (decode batches) and the shrink: smaller tiles so enough blocks
+// exist to fill the CUs.
+using MainBig = Tile<256, 256, 2, 4>;
 using MainSmall = Tile<64, 64, 2, 2>;
 using ShrinkBig = Tile<128, 128, 2, 2>;
 using ShrinkSmall = Tile<64, 64, 2, 2>;
