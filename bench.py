@@ -120,7 +120,7 @@ class StepRunner:
         M = layers[0][0]["X"].shape[0]
         self.M, self.Ma = M, adapter_rows(seg_starts, seg_adapter)
         self.seg_starts, self.seg_adapter, self.scale = list(seg_starts), list(seg_adapter), scale
-        ws = max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK) for p in layers[0])
+        ws = max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, 1) for p in layers[0])
         self.workspace = torch.empty(ws, dtype=torch.uint8, device=dev)
         self.outs = {}
         for projs in layers:

@@ -93,9 +93,9 @@ typedef enum lora_dtype {
  *   rank         r, shared by all adapters of the call (ignored when no row names an adapter)
  *   scale        s, applied to the adapter term of every adapter row
  *   Y            device, M x N, fully overwritten; must not overlap X, W, any A/B or the workspace
- *   workspace    device scratch of at least lora_proj_workspace_bytes(M, N, K, rank, dtype)
- *                bytes (may be NULL with size 0 when no row names an adapter); its contents
- *                are not preserved
+ *   workspace    device scratch of at least lora_proj_workspace_bytes(M, N, K, rank,
+ *                n_adapters, dtype) bytes (may be NULL with size 0 when that is 0); its
+ *                contents are not preserved
  *   stream       HIP stream the work is ordered on (0 = the null stream)
  */
 lora_status lora_proj(const void* X,
@@ -114,8 +114,10 @@ lora_status lora_proj(const void* X,
  *
  * Identical arguments, checks and results; in addition, when main_start or
  * main_stop is not NULL it is recorded on `stream` at the start / end of the
- * output kernel (the base product with the adapter expand and the store),
- * which is the call's dominant kernel, so that it can be timed on its own.
+ * call's dominant work, so that it can be timed on its own: for batches of
+ * more than 128 rows, the output kernel (base product with the adapter expand
+ * and the store; the shrink before it is excluded); for smaller batches, both
+ * kernels of the call (split-K streaming of W and A, then the finish).
  * The events belong to the caller and must have been created on the current
  * device.
  */
@@ -131,11 +133,15 @@ lora_status lora_proj_ex(const void* X,
                          hipStream_t stream,
                          hipEvent_t main_start, hipEvent_t main_stop);
 
-/* Workspace bytes lora_proj needs for any segment table of this shape (an upper bound).
- * Returns 0 for invalid arguments. */
-size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype);
+/* Workspace bytes lora_proj needs for any segment table of this shape that names at most
+ * n_adapters adapters (an upper bound).  Returns 0 for invalid arguments.  Batches of at most
+ * 128 rows (the decode path) always need a workspace, for split-K partial sums; larger batches
+ * need one only when some row names an adapter. */
+size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
+                                 lora_dtype dtype);
 
-/* Name of the kernel path lora_proj takes for this shape: "prefill", "decode" or "f32"
+/* Name of the kernel path lora_proj takes for this shape: "prefill" (more than 128 rows),
+ * "decode" (at most 128 rows) or "f32" (test mode)
  * ("invalid" for arguments lora_proj would reject).  A pure function of its arguments. */
 const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype);
 

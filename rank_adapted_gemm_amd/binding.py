@@ -49,7 +49,7 @@ def load():
     lib.lora_proj.restype = ctypes.c_int
     lib.lora_proj_ex.argtypes = lib.lora_proj.argtypes + [vp, vp]
     lib.lora_proj_ex.restype = ctypes.c_int
-    lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, ctypes.c_int]
+    lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
     lib.lora_proj_path.restype = ctypes.c_char_p
@@ -63,8 +63,8 @@ def status_string(status: int) -> str:
     return load().lora_status_string(status).decode()
 
 
-def workspace_bytes(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> int:
-    return int(load().lora_proj_workspace_bytes(M, N, K, rank, DTYPES[dtype]))
+def workspace_bytes(M: int, N: int, K: int, rank: int, n_adapters: int = 1, dtype: str = "bf16") -> int:
+    return int(load().lora_proj_workspace_bytes(M, N, K, rank, n_adapters, DTYPES[dtype]))
 
 
 def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:
@@ -117,7 +117,7 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
         out = torch.empty((M, N), dtype=out_t, device=X.device)
     if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
         raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
-    need = workspace_bytes(M, N, K, rank, dtype) if rank else 0
+    need = workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype)
     if workspace is None and need:
         workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None

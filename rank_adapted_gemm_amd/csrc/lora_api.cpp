@@ -52,6 +52,14 @@ bool rank_ok(int64_t rank) {
 
 bool small_m(int64_t M) { return M <= lora::kDecodeMaxRows; }
 
+// Workspace of a call: the decode path keeps split-K partials for W and for each
+// adapter named in the batch; the prefill path keeps s X A^T (4 bytes per
+// element, bf16 hi + lo or fp32) for adapter rows, indexed by global row.
+size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used, lora_dtype dtype) {
+  if (dtype != LORA_F32 && small_m(M)) return lora::decode_workspace_bytes(M, N, K, n_used ? rank : 0, n_used);
+  return n_used ? t_bytes(M, rank) : 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -69,9 +77,13 @@ const char* lora_status_string(lora_status s) {
   return "unknown status";
 }
 
-size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype) {
-  if (check_shape(M, N, K, dtype) != LORA_OK || !rank_ok(rank)) return 0;
-  return t_bytes(M, rank);
+size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
+                                 lora_dtype dtype) {
+  if (check_shape(M, N, K, dtype) != LORA_OK) return 0;
+  if (n_adapters < 0 || n_adapters > LORA_MAX_ADAPTERS) return 0;
+  if (n_adapters > 0 && !rank_ok(rank)) return 0;
+  const int64_t n_used = std::min<int64_t>(n_adapters, std::max<int64_t>(M, 1));
+  return need_bytes(M, N, K, rank, n_used, dtype);
 }
 
 const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype) {
@@ -149,7 +161,17 @@ lora_status lora_proj_ex(const void* X,
   }
 
   // ---- workspace
-  const size_t need = has_adapter ? t_bytes(M, rank) : 0;
+  int n_used = 0;
+  int8_t slot_of[LORA_MAX_ADAPTERS];
+  int8_t slot_adapter[LORA_MAX_ADAPTERS] = {};
+  for (int a = 0; a < LORA_MAX_ADAPTERS; ++a) slot_of[a] = -1;
+  for (int a = 0; a < n_adapters; ++a)
+    if (used[a]) {
+      slot_of[a] = int8_t(n_used);
+      slot_adapter[n_used++] = int8_t(a);
+    }
+  const bool decode = dtype != LORA_F32 && small_m(M);
+  const size_t need = need_bytes(M, N, K, rank, n_used, dtype);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return LORA_EWORKSPACE;
     if (!aligned16(workspace)) return LORA_EINVAL;
@@ -177,7 +199,7 @@ lora_status lora_proj_ex(const void* X,
   p.X = X;
   p.W = W;
   p.Y = Y;
-  p.T = has_adapter ? workspace : nullptr;
+  p.T = has_adapter && !decode ? workspace : nullptr;
   p.M = int32_t(M);
   p.N = int32_t(N);
   p.K = int32_t(K);
@@ -186,19 +208,60 @@ lora_status lora_proj_ex(const void* X,
   p.x_bytes = uint32_t(x_bytes);
   p.w_bytes = uint32_t(w_bytes);
   p.y_bytes = uint32_t(y_bytes);
-  p.t_bytes = uint32_t(need);
+  p.t_bytes = decode ? 0u : uint32_t(need);
   p.a_bytes = uint32_t(a_bytes);
   p.b_bytes = uint32_t(b_bytes);
 
   hipError_t e = hipSuccess;
-  if (dtype == LORA_F32) {
+  if (decode) {
+    const lora::DecodeSplit sp = lora::decode_split(N, K);
+    lora::DecodeArgs d;
+    memset(&d, 0, sizeof(d));
+    d.X = X;
+    d.W = W;
+    d.Y = Y;
+    d.P = static_cast<float*>(workspace);
+    d.M = int32_t(M);
+    d.N = int32_t(N);
+    d.K = int32_t(K);
+    d.rank = has_adapter ? rank : 0;
+    d.scale = scale;
+    d.nstages = sp.nstages;
+    d.S = sp.S;
+    d.sc = sp.sc;
+    d.n_wtiles = int32_t((N + lora::kDecodeTile - 1) / lora::kDecodeTile);
+    d.n_atiles = has_adapter ? (rank + lora::kDecodeTile - 1) / lora::kDecodeTile : 0;
+    d.n_used = n_used;
+    const size_t p_bytes = size_t(sp.S) * size_t(M) * size_t(N) * 4;
+    const size_t pt_bytes = size_t(sp.S) * size_t(M) * size_t(n_used) * size_t(d.rank) * 4;
+    const size_t th_bytes = size_t(n_used) * size_t(M) * size_t(d.rank) * 2;
+    char* ws = static_cast<char*>(workspace);
+    const size_t o_pt = (p_bytes + 255) & ~size_t(255);
+    const size_t o_th = (o_pt + pt_bytes + 255) & ~size_t(255);
+    const size_t o_tl = (o_th + th_bytes + 255) & ~size_t(255);
+    d.PT = reinterpret_cast<float*>(ws + o_pt);
+    d.TH = reinterpret_cast<uint16_t*>(ws + o_th);
+    d.TL = reinterpret_cast<uint16_t*>(ws + o_tl);
+    d.x_bytes = uint32_t(x_bytes);
+    d.w_bytes = uint32_t(w_bytes);
+    d.y_bytes = uint32_t(y_bytes);
+    d.a_bytes = uint32_t(a_bytes);
+    d.b_bytes = uint32_t(b_bytes);
+    d.p_bytes = uint32_t(p_bytes);
+    d.pt_bytes = uint32_t(pt_bytes);
+    d.t_bytes = uint32_t(th_bytes);
+    for (int g = 0; g < tbl.n; ++g)
+      for (int32_t m = tbl.start[g]; m < tbl.start[g + 1]; ++m)
+        d.row_slot[m] = tbl.adapter[g] < 0 ? int8_t(-1) : slot_of[tbl.adapter[g]];
+    for (int i = 0; i < n_used; ++i) d.slot_adapter[i] = slot_adapter[i];
+    e = lora::launch_decode(d, at, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
+  } else if (dtype == LORA_F32) {
     if (has_adapter) e = lora::launch_f32_shrink(p, tbl, at, stream);
     if (e == hipSuccess) e = lora::launch_f32_main(p, tbl, at, has_adapter, stream, main_start, main_stop);
   } else {
-    const bool sm = small_m(M);
-    if (has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, sm, stream);
+    if (has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, false, stream);
     if (e == hipSuccess)
-      e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, sm, stream, main_start,
+      e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, false, stream, main_start,
                                  main_stop);
   }
   return e == hipSuccess ? LORA_OK : LORA_EHIP;

@@ -22,32 +22,14 @@
 // Every global access goes through a buffer descriptor sized to its operand:
 // masked or out-of-range loads return zero and out-of-range stores are
 // dropped by the hardware.
-#include "lora_internal.h"
+#include "lora_device.h"
 
 namespace lora {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
 constexpr int BK = 32;          // K elements per LDS stage (64 bytes per tile row)
 constexpr int ROW_BYTES = BK * 2;
 constexpr int NSTAGE = 4;       // LDS ring depth; NSTAGE - 1 stages are in flight
-
-typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  // word3 0x00020000: raw 32-bit data, no swizzle (gfx9 family)
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
-
-// The same descriptor as four words, for the inline-assembly loads.
-__device__ __forceinline__ i32x4 make_rsrc_words(const void* p, uint32_t bytes) {
-  const uint64_t a = reinterpret_cast<uint64_t>(p);
-  return i32x4{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xFFFFu), int32_t(bytes), 0x00020000};
-}
 
 // One operand of a K-loop: rows of a row-major bf16 matrix whose reduction
 // index is contiguous.  Tile row i is global row row0 + i.  Rows past the
@@ -82,21 +64,6 @@ struct Tile {
 // four distinct slots, so no two lanes of a cycle share a bank.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ ((r >> 2) & 3)) << 4); }
 
-// Global -> LDS: one buffer_load_dwordx4 with the lds flag writes 64 lanes x
-// 16 bytes contiguously at M0, i.e. 16 tile rows; lane l fills row l/4, slot
-// l%4 and so fetches the chunk that the swizzle puts there.  Issued from
-// inline assembly (M0 is set in the same statement), so completion is tracked
-// by the explicit vmcnt waits of the K-loop.
-__device__ __forceinline__ void dma16(const i32x4& res, uint32_t voff, uint32_t lds_addr) {
-  const i32x4 r{__builtin_amdgcn_readfirstlane(res[0]), __builtin_amdgcn_readfirstlane(res[1]),
-                __builtin_amdgcn_readfirstlane(res[2]), __builtin_amdgcn_readfirstlane(res[3])};
-  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r),
-               "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
-}
-
-template <int N>
-__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
-
 // Wait until at most `stages` later stages of PW loads each are still in flight.
 template <int PW>
 __device__ __forceinline__ void wait_stages(int stages) {
@@ -109,8 +76,7 @@ __device__ __forceinline__ void wait_stages(int stages) {
 
 template <class C>
 __device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane) {
-  // LDS byte offset of the stage (M0 takes LDS addresses, not flat ones)
-  const uint32_t base = uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) char*)stage));
+  const uint32_t base = lds_addr(stage);
 #pragma unroll
   for (int i = 0; i < C::PW; ++i) {
     const int g = wave * C::PW + i;                 // 16-row group of the stage (uniform)
@@ -318,22 +284,6 @@ __device__ __forceinline__ void tile_of_block(int b, int ntn, int ntm, int& tn, 
   tn = in / gsz;
 }
 
-// First segment whose rows reach past row m (segments are non-empty and sorted).
-__device__ __forceinline__ int first_segment(const SegTable& st, int m) {
-  int lo = 0, hi = st.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (st.start[mid] <= m) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
-__device__ __forceinline__ uint32_t bf16_bits(float f) {
-  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
-}
-
-__device__ __forceinline__ uint32_t pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
-
 // ------------------------------------------------------------------ shrink
 // Grid: one block per (rank tile, row tile).  For every adapter segment that
 // overlaps the block's rows: acc = A_a[rank tile] X[rows]^T, then
@@ -380,12 +330,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
           const int jr = j0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
           float h[4], l[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float t = p.scale * acc[i][j][q * 4 + e];
-            const __bf16 hb = static_cast<__bf16>(t);
-            h[e] = static_cast<float>(hb);
-            l[e] = t - h[e];            // exact: t and bf16(t) share their leading bits
-          }
+          for (int e = 0; e < 4; ++e) split_hi_lo(p.scale * acc[i][j][q * 4 + e], h[e], l[e]);
           const uint32_t off = (row_ok && jr < p.rank) ? (uint32_t(m) * uint32_t(p.rank) + uint32_t(jr)) * 2u
                                                        : kMaskedOffset;
           const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};

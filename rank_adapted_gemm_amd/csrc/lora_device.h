@@ -1,0 +1,67 @@
+// Device helpers shared by the bf16 kernels (prefill and decode paths).
+#pragma once
+
+#include "lora_internal.h"
+
+namespace lora {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
+  // word3 0x00020000: raw 32-bit data, no swizzle (gfx9 family)
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+
+// The same descriptor as four words, for the inline-assembly loads.
+__device__ __forceinline__ i32x4 make_rsrc_words(const void* p, uint32_t bytes) {
+  const uint64_t a = reinterpret_cast<uint64_t>(p);
+  return i32x4{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xFFFFu), int32_t(bytes), 0x00020000};
+}
+
+// Global -> LDS: one buffer_load_dwordx4 with the lds flag writes 64 lanes x
+// 16 bytes contiguously at M0.  Issued from inline assembly (M0 is set in the
+// same statement), so completion is tracked by explicit vmcnt waits.
+__device__ __forceinline__ void dma16(const i32x4& res, uint32_t voff, uint32_t lds_addr) {
+  const i32x4 r{__builtin_amdgcn_readfirstlane(res[0]), __builtin_amdgcn_readfirstlane(res[1]),
+                __builtin_amdgcn_readfirstlane(res[2]), __builtin_amdgcn_readfirstlane(res[3])};
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" : : "v"(voff), "s"(r),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
+
+// LDS byte offset of a pointer into a __shared__ array (M0 takes LDS addresses).
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return uint32_t(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// First segment whose rows reach past row m (segments are non-empty and sorted).
+__device__ __forceinline__ int first_segment(const SegTable& st, int m) {
+  int lo = 0, hi = st.n - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (st.start[mid] <= m) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__device__ __forceinline__ uint32_t bf16_bits(float f) {
+  return uint32_t(__builtin_bit_cast(uint16_t, static_cast<__bf16>(f)));
+}
+
+__device__ __forceinline__ uint32_t pack2(float a, float b) { return bf16_bits(a) | (bf16_bits(b) << 16); }
+
+// hi = bf16(t), lo = bf16(t - hi): t - hi is exact in fp32 (the two share
+// their leading bits), so hi + lo carries t to about 2^-17 relative.
+__device__ __forceinline__ void split_hi_lo(float t, float& hi, float& lo) {
+  hi = static_cast<float>(static_cast<__bf16>(t));
+  lo = t - hi;
+}
+
+}  // namespace lora

@@ -59,10 +59,16 @@ def test_status_strings():
 
 
 def test_workspace_and_path_queries():
-    assert bd.workspace_bytes(16384, 5120, 5120, 256) == 16384 * 256 * 4
-    assert bd.workspace_bytes(70, 17408, 5120, 256, "f32") == 70 * 256 * 4
+    assert bd.workspace_bytes(16384, 5120, 5120, 256) == 16384 * 256 * 4       # prefill: s X A^T
+    assert bd.workspace_bytes(16384, 5120, 5120, 256, 0) == 0                  # prefill, base only
+    assert bd.workspace_bytes(70, 17408, 5120, 256, dtype="f32") == 70 * 256 * 4
     assert bd.workspace_bytes(64, 512, 250, 16) == 0          # K not a multiple of 8
     assert bd.workspace_bytes(64, 512, 256, 24) == 0          # rank not a multiple of 16
+    # decode (<= 128 rows): split-K partials of W always, plus adapter partials
+    base = bd.workspace_bytes(70, 5120, 5120, 256, 0)
+    one = bd.workspace_bytes(70, 5120, 5120, 256, 1)
+    two = bd.workspace_bytes(70, 5120, 5120, 256, 2)
+    assert 0 < base < one < two and base % 256 == 0 and base >= 70 * 5120 * 4
     assert bd.path(16384, 5120, 5120, 256) == "prefill"
     assert bd.path(70, 5120, 5120, 256) == "decode"
     assert bd.path(128, 5120, 5120, 256) == "decode"
@@ -74,7 +80,7 @@ def test_workspace_and_path_queries():
 def call(**kw):
     a = dict(X=FAKE, seg_starts=[0, 32, 64], seg_adapter=[-1, 0], W=FAKE2, A=[FAKE3], B=[FAKE4], rank=16,
              scale=0.5, Y=FAKE5, M=64, N=512, K=256, dtype="bf16", workspace=FAKE * 320,
-             workspace_bytes_=64 * 16 * 4, stream=None)
+             workspace_bytes_=1 << 24, stream=None)
     a.update(kw)
     return bd.lora_proj_raw(**a)
 
@@ -103,7 +109,8 @@ def call(**kw):
     (dict(B=[None]), bd.LORA_EADAPTER),
     (dict(A=[FAKE3 + 4]), bd.LORA_EINVAL),
     (dict(workspace=None, workspace_bytes_=0), bd.LORA_EWORKSPACE),
-    (dict(workspace_bytes_=64 * 16 * 4 - 1), bd.LORA_EWORKSPACE),
+    (dict(workspace_bytes_=64 * 16 * 4), bd.LORA_EWORKSPACE),            # below the decode partials
+    (dict(M=300, seg_starts=[0, 32, 300], workspace_bytes_=300 * 16 * 4 - 1), bd.LORA_EWORKSPACE),
     (dict(Y=FAKE + 4096), bd.LORA_EINVAL),                               # Y overlaps X
     (dict(Y=FAKE2 + 4096), bd.LORA_EINVAL),                              # Y overlaps W
     (dict(Y=FAKE3), bd.LORA_EINVAL),                                     # Y overlaps A
