@@ -77,6 +77,9 @@ typedef enum lora_dtype {
 #define LORA_MAX_ADAPTERS 32
 #define LORA_MIN_RANK 16
 #define LORA_MAX_RANK 512
+/* Bytes at the start of every workspace reserved for the decode path's
+ * counters (see lora_proj's `workspace`). */
+#define LORA_WORKSPACE_COUNTER_BYTES 65536
 
 /*
  * lora_proj — one projection call over a batch of rows from several requests.
@@ -94,8 +97,12 @@ typedef enum lora_dtype {
  *   scale        s, applied to the adapter term of every adapter row
  *   Y            device, M x N, fully overwritten; must not overlap X, W, any A/B or the workspace
  *   workspace    device scratch of at least lora_proj_workspace_bytes(M, N, K, rank,
- *                n_adapters, dtype) bytes (may be NULL with size 0 when that is 0); its
- *                contents are not preserved
+ *                n_adapters, dtype) bytes (may be NULL with size 0 when that is 0).  Its
+ *                first LORA_WORKSPACE_COUNTER_BYTES are a counter area that the blocks of
+ *                one launch use to hand work to each other: it must be all zero before the
+ *                first call that uses the workspace (allocate it zero-filled), and every
+ *                call leaves it zero again.  A non-zero counter area gives wrong results,
+ *                never a hang.  The rest is scratch whose contents are not preserved
  *   stream       HIP stream the work is ordered on (0 = the null stream)
  */
 lora_status lora_proj(const void* X,
@@ -116,8 +123,8 @@ lora_status lora_proj(const void* X,
  * main_stop is not NULL it is recorded on `stream` at the start / end of the
  * call's dominant work, so that it can be timed on its own: for batches of
  * more than 128 rows, the output kernel (base product with the adapter expand
- * and the store; the shrink before it is excluded); for smaller batches, both
- * kernels of the call (split-K streaming of W and A, then the finish).
+ * and the store; the shrink before it is excluded); for smaller batches, the
+ * call's single kernel.
  * The events belong to the caller and must have been created on the current
  * device.
  */
@@ -134,9 +141,10 @@ lora_status lora_proj_ex(const void* X,
                          hipEvent_t main_start, hipEvent_t main_stop);
 
 /* Workspace bytes lora_proj needs for any segment table of this shape that names at most
- * n_adapters adapters (an upper bound).  Returns 0 for invalid arguments.  Batches of at most
- * 128 rows (the decode path) always need a workspace, for split-K partial sums; larger batches
- * need one only when some row names an adapter. */
+ * n_adapters adapters (an upper bound), counter area included.  Returns 0 for invalid
+ * arguments.  Batches of at most 128 rows (the decode path) always need a workspace, for its
+ * counters and split-K partial sums; larger batches need one only when some row names an
+ * adapter. */
 size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
                                  lora_dtype dtype);
 

@@ -18,6 +18,7 @@ STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESEGMENTS", 3: "LORA_EA
                 4: "LORA_EUNSUPPORTED", 5: "LORA_EWORKSPACE", 6: "LORA_EHIP"}
 DTYPES = {"bf16": 0, "f32": 1, "bf16_f32out": 2}
 MAX_SEGMENTS, MAX_ADAPTERS, MIN_RANK, MAX_RANK = 256, 32, 16, 512
+WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
 EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_workspace_bytes", "lora_proj_path", "lora_status_string")
 
 _lib = None
@@ -118,8 +119,8 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
     if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
         raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
     need = workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype)
-    if workspace is None and need:
-        workspace = torch.empty(need, dtype=torch.uint8, device=X.device)
+    if workspace is None and need:   # zero-filled: the counter area must start at zero
+        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
     if stream is None:

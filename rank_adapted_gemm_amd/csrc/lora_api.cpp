@@ -36,10 +36,15 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// The decode path's counters (one per 128 output columns, plus three) must fit
+// the workspace's counter area.
+bool decode_counters_fit(int64_t N) { return ((N + 127) / 128 + 3) * 8 <= LORA_WORKSPACE_COUNTER_BYTES; }
+
 lora_status check_shape(int64_t M, int64_t N, int64_t K, lora_dtype dtype) {
   if (!dtype_ok(dtype)) return LORA_EUNSUPPORTED;
   if (M < 0 || N < 1 || K < 1) return LORA_EINVAL;
   if (K % 8 != 0) return LORA_EUNSUPPORTED;
+  if (dtype != LORA_F32 && M <= lora::kDecodeMaxRows && !decode_counters_fit(N)) return LORA_EUNSUPPORTED;
   const int64_t ie = int64_t(in_elem_bytes(dtype)), oe = int64_t(out_elem_bytes(dtype));
   if (M * K * ie >= kMaxOperandBytes || N * K * ie >= kMaxOperandBytes || M * N * oe >= kMaxOperandBytes)
     return LORA_EUNSUPPORTED;
@@ -52,12 +57,18 @@ bool rank_ok(int64_t rank) {
 
 bool small_m(int64_t M) { return M <= lora::kDecodeMaxRows; }
 
+// The decode split is planned for the call's rank even when no row names an
+// adapter (a call without adapters may pass any rank).
+int64_t plan_rank(int64_t rank) { return rank_ok(rank) ? rank : 256; }
+
+
+
 // Workspace of a call: the decode path keeps split-K partials for W and for each
 // adapter named in the batch; the prefill path keeps s X A^T (4 bytes per
 // element, bf16 hi + lo or fp32) for adapter rows, indexed by global row.
 size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used, lora_dtype dtype) {
-  if (dtype != LORA_F32 && small_m(M)) return lora::decode_workspace_bytes(M, N, K, n_used ? rank : 0, n_used);
-  return n_used ? t_bytes(M, rank) : 0;
+  if (dtype != LORA_F32 && small_m(M)) return lora::decode_plan(M, N, K, plan_rank(rank), n_used).total;
+  return n_used ? LORA_WORKSPACE_COUNTER_BYTES + t_bytes(M, rank) : 0;
 }
 
 }  // namespace
@@ -199,7 +210,7 @@ lora_status lora_proj_ex(const void* X,
   p.X = X;
   p.W = W;
   p.Y = Y;
-  p.T = has_adapter && !decode ? workspace : nullptr;
+  p.T = has_adapter && !decode ? static_cast<char*>(workspace) + LORA_WORKSPACE_COUNTER_BYTES : nullptr;
   p.M = int32_t(M);
   p.N = int32_t(N);
   p.K = int32_t(K);
@@ -208,53 +219,54 @@ lora_status lora_proj_ex(const void* X,
   p.x_bytes = uint32_t(x_bytes);
   p.w_bytes = uint32_t(w_bytes);
   p.y_bytes = uint32_t(y_bytes);
-  p.t_bytes = decode ? 0u : uint32_t(need);
+  p.t_bytes = has_adapter && !decode ? uint32_t(t_bytes(M, rank)) : 0u;
   p.a_bytes = uint32_t(a_bytes);
   p.b_bytes = uint32_t(b_bytes);
 
   hipError_t e = hipSuccess;
   if (decode) {
-    const lora::DecodeSplit sp = lora::decode_split(N, K);
+    const lora::DecodePlan pl = lora::decode_plan(M, N, K, plan_rank(rank), n_used);
     lora::DecodeArgs d;
     memset(&d, 0, sizeof(d));
+    char* ws = static_cast<char*>(workspace);
     d.X = X;
     d.W = W;
     d.Y = Y;
-    d.P = static_cast<float*>(workspace);
-    d.M = int32_t(M);
-    d.N = int32_t(N);
-    d.K = int32_t(K);
-    d.rank = has_adapter ? rank : 0;
-    d.scale = scale;
-    d.nstages = sp.nstages;
-    d.S = sp.S;
-    d.sc = sp.sc;
-    d.n_wtiles = int32_t((N + lora::kDecodeTile - 1) / lora::kDecodeTile);
-    d.n_atiles = has_adapter ? (rank + lora::kDecodeTile - 1) / lora::kDecodeTile : 0;
-    d.n_used = n_used;
-    const size_t p_bytes = size_t(sp.S) * size_t(M) * size_t(N) * 4;
-    const size_t pt_bytes = size_t(sp.S) * size_t(M) * size_t(n_used) * size_t(d.rank) * 4;
-    const size_t th_bytes = size_t(n_used) * size_t(M) * size_t(d.rank) * 2;
-    char* ws = static_cast<char*>(workspace);
-    const size_t o_pt = (p_bytes + 255) & ~size_t(255);
-    const size_t o_th = (o_pt + pt_bytes + 255) & ~size_t(255);
-    const size_t o_tl = (o_th + th_bytes + 255) & ~size_t(255);
-    d.PT = reinterpret_cast<float*>(ws + o_pt);
-    d.TH = reinterpret_cast<uint16_t*>(ws + o_th);
-    d.TL = reinterpret_cast<uint16_t*>(ws + o_tl);
+    d.cnt = reinterpret_cast<unsigned long long*>(ws + pl.off_cnt);
+    d.PA = reinterpret_cast<float*>(ws + pl.off_pa);
+    d.PW = reinterpret_cast<float*>(ws + pl.off_pw);
+    d.PE = reinterpret_cast<float*>(ws + pl.off_pe);
+    d.TH = reinterpret_cast<uint16_t*>(ws + pl.off_th);
+    d.TL = reinterpret_cast<uint16_t*>(ws + pl.off_tl);
     d.x_bytes = uint32_t(x_bytes);
     d.w_bytes = uint32_t(w_bytes);
     d.y_bytes = uint32_t(y_bytes);
     d.a_bytes = uint32_t(a_bytes);
     d.b_bytes = uint32_t(b_bytes);
-    d.p_bytes = uint32_t(p_bytes);
-    d.pt_bytes = uint32_t(pt_bytes);
-    d.t_bytes = uint32_t(th_bytes);
+    d.t_bytes = uint32_t(pl.t_bytes);
+    d.pa_bytes = uint32_t(pl.pa_bytes);
+    d.pw_bytes = uint32_t(pl.pw_bytes);
+    d.pe_bytes = uint32_t(pl.pe_bytes);
+    d.M = int32_t(M);
+    d.N = int32_t(N);
+    d.K = int32_t(K);
+    d.rank = int32_t(plan_rank(rank));
+    d.scale = scale;
+    d.nst = pl.nst;
+    d.nrs = pl.nrs;
+    d.n_used = pl.n_used;
+    d.ntA = pl.ntA;
+    d.ntW = pl.ntW;
+    d.GA = pl.GA;
+    d.GW = pl.GW;
+    d.smaxA = pl.smaxA;
+    d.smaxW = pl.smaxW;
+    d.smaxE = pl.smaxE;
     for (int g = 0; g < tbl.n; ++g)
       for (int32_t m = tbl.start[g]; m < tbl.start[g + 1]; ++m)
         d.row_slot[m] = tbl.adapter[g] < 0 ? int8_t(-1) : slot_of[tbl.adapter[g]];
     for (int i = 0; i < n_used; ++i) d.slot_adapter[i] = slot_adapter[i];
-    e = lora::launch_decode(d, at, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
+    e = lora::launch_decode(d, at, pl.MT, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
   } else if (dtype == LORA_F32) {
     if (has_adapter) e = lora::launch_f32_shrink(p, tbl, at, stream);
     if (e == hipSuccess) e = lora::launch_f32_main(p, tbl, at, has_adapter, stream, main_start, main_stop);

@@ -1,405 +1,538 @@
-// Decode-path kernels of the mixed-adapter LoRA projection (M <= 128 rows).
+// Decode-path kernel of the mixed-adapter LoRA projection (M <= 128 rows).
 //
-// At decode sizes the call is bound by HBM: every byte of W, A_a and B_a is
-// read once and reused only M times.  Three launches:
+// At decode sizes the call is bound by HBM: every byte of W, A_a and B_a is read
+// once and reused only M times.  One launch does the whole call:
 //
-//   partial  One block per (64-row tile, K split) of W and of each used
-//            adapter's A; every tile uses the same K split, so all blocks do
-//            the same work.  A block streams its slab of W (or A) and the
-//            matching K-range of X through an LDS ring in full 128-byte rows
-//            (buffer_load ... lds) and multiplies on MFMA; fp32 partial sums go
-//            to the workspace.
-//   reduce   T = s * (sum of the A partials) on the rows of each adapter, zero
-//            on other rows, stored as bf16 hi = bf16(T) and lo = bf16(T - hi).
-//   finish   One block per 64 output columns: acc = sum of the W partials in
-//            split order, acc += T_hi B_a^T + T_lo B_a^T on MFMA, one store.
+//   * Work is cut into units: one unit is a 64-element K slice (128-byte rows)
+//     of a 128-row tile of a weight matrix, multiplied against the same slice
+//     of the activation rows.  A unit streams through an LDS ring filled by
+//     buffer_load ... lds (full 128-byte lines, several units in flight), and
+//     all four waves multiply on v_mfma_f32_16x16x32_bf16 (32 weight rows x
+//     16*MT activation rows each).
+//   * A blocks (first in the grid, a few) each take one K range of every A_a
+//     tile and store one fp32 partial per tile.  When all of them are done
+//     they reduce T = s * X A^T between them, each a share of the
+//     (tile, 16-row) pieces, and store it as bf16 hi = bf16(T), lo =
+//     bf16(T - hi), zero on rows that name another adapter or none.
+//   * W blocks (one per remaining CU) split the W units evenly and in order
+//     (stream-K), then their share of the expand units: B_a's rows against
+//     T_hi and T_lo.  By then T is normally done; if not, they wait for it.
+//   * At the end of its part of a W tile a block stores its fp32 partial
+//     (fragment-major, so stores and reloads are whole 1 KiB lines) and counts
+//     itself in on the tile.  The last one in sums the tile's W partials and
+//     then its expand partials, in block order (so the result does not depend
+//     on timing), and stores Y once.
 //
-// "Two 27B models on a single RTX 5090", section 4 request-path figure: the
-// adapter's two thin matrices run only for requests that name it; base-only
-// rows get T = 0 and therefore exactly their base sum.
+// The split of the W units depends on (N, K, r) only, and the expand adds exact
+// zeros on rows that name no adapter, so base-only rows come out bitwise the
+// same with or without adapter rows in the batch ("two 27B models on a single
+// RTX 5090", section 4 request-path figure: requests naming the base model use
+// the base weights alone).
+//
+// Data shared between blocks (partials, T) is written and read with
+// device-scope (sc1) accesses, so handing it over costs a vmcnt wait and one
+// atomic add, never an L2 flush.  The counters sit in the workspace's counter
+// area: zero when the workspace is first used, and put back to zero by the
+// block that uses each last, so nothing has to clear them between calls.
 #include <algorithm>
+#include <cmath>
 
 #include "lora_device.h"
 
 namespace lora {
-
-DecodeSplit decode_split(int64_t N, int64_t K) {
-  DecodeSplit d;
-  d.nstages = int((K + kDecodeStageK - 1) / kDecodeStageK);
-  const int64_t ntiles = (N + kDecodeTile - 1) / kDecodeTile;
-  int S = int((kDecodeTargetBlocks + ntiles / 2) / ntiles);
-  S = std::max(1, std::min(S, d.nstages));
-  d.sc = (d.nstages + S - 1) / S;
-  d.S = (d.nstages + d.sc - 1) / d.sc;
-  return d;
-}
-
-static size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
-
-size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used) {
-  const DecodeSplit sp = decode_split(N, K);
-  const size_t p = round256(size_t(sp.S) * size_t(M) * size_t(N) * 4);
-  const size_t pt = round256(size_t(sp.S) * size_t(M) * size_t(n_used) * size_t(rank) * 4);
-  const size_t t = round256(size_t(n_used) * size_t(M) * size_t(rank) * 2);
-  return p + pt + 2 * t;
-}
-
 namespace {
 
-constexpr int DTN = kDecodeTile;                 // W / A rows per partial tile; columns per finish tile
-constexpr int DROW = kDecodeStageK * 2;          // bytes per tile row per stage: one full 128-byte line
+constexpr int TR = kDecodeTileRows;   // 128 weight rows per tile
+constexpr int UK = kDecodeUnitK;      // 64 elements per unit
+constexpr int RB = UK * 2;            // 128 bytes per tile row per unit
 
-// 16-byte chunk c of a 128-byte row r sits at slot c ^ ((r >> 1) & 7): the 16
-// lanes a ds_read_b128 serves per cycle read one chunk of 16 consecutive rows,
-// and the XOR spreads each parity's eight rows over eight slots, so the 64
-// banks see no conflict.
-__device__ __forceinline__ int doff(int r, int c) { return r * DROW + ((c ^ ((r >> 1) & 7)) << 4); }
+__host__ __device__ inline int64_t pstart(int64_t b, int64_t U, int64_t G) { return b * U / G; }
+// Block of a partition of U units over G blocks that holds unit u.
+__host__ __device__ inline int64_t pblock(int64_t u, int64_t U, int64_t G) { return ((u + 1) * G - 1) / U; }
 
-__device__ __forceinline__ bf16x8 dfrag(const char* base, int r, int c) {
+template <int MT_>
+struct DG {
+  static constexpr int MT = MT_;                   // 16-row activation tiles
+  static constexpr int XR = 16 * MT;               // activation rows staged per unit
+  static constexpr int STAGE = (TR + XR) * RB;
+  static constexpr int NS = std::min(8, (160 * 1024) / STAGE);
+  static constexpr int GT = (TR + XR) / 8;         // 8-row groups, one wave-wide 16-byte load each
+  static constexpr int NA = GT % 4 == 0 ? 4 : GT % 4;
+  static constexpr int PWA = (GT + 3) / 4;         // loads per unit, waves < NA
+  static constexpr int PWB = GT / 4;               // loads per unit, other waves
+  static constexpr int FRAG = 4 * 2 * MT * 64 * 16;   // bytes of one partial
+  static_assert(NS >= 3, "ring too shallow");
+};
+
+// 16-byte chunk c of a 128-byte row r sits at slot c ^ ((r >> 1) & 7).  A
+// ds_read_b128 serves 16 lanes per cycle: rows r..r+15 of one chunk, which this
+// spreads over all 64 banks.
+__device__ __forceinline__ int doff(int r, int c) { return r * RB + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ bf16x8 frag(const char* base, int r, int c) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + doff(r, c)));
 }
 
-// Partial-kernel geometry for TM activation rows (M <= TM).  The ring gets as
-// many slots as fit in 80 KiB, so two blocks share a CU.
-template <int TM_>
-struct DGeo {
-  static constexpr int TM = TM_;
-  static constexpr int FM = TM / 32;
-  static constexpr int STAGE = (DTN + TM) * DROW;
-  static constexpr int NS = (80 * 1024) / STAGE;
-  static constexpr int GROUPS = STAGE / 1024;    // 8-row groups, one wave-wide load each
-  static constexpr int PW = GROUPS / 4;          // loads per wave per stage
-  static_assert(GROUPS % 4 == 0 && NS >= 3, "stage must split over four waves and leave a 3-slot ring");
+template <int PW, int NS>
+__device__ __forceinline__ void wait_ring(int ahead) {   // at most `ahead` later units still loading
+  if constexpr (NS > 7) { if (ahead >= 6) { wait_vm<PW * 6>(); return; } }
+  if constexpr (NS > 6) { if (ahead >= 5) { wait_vm<PW * 5>(); return; } }
+  if constexpr (NS > 5) { if (ahead >= 4) { wait_vm<PW * 4>(); return; } }
+  if constexpr (NS > 4) { if (ahead >= 3) { wait_vm<PW * 3>(); return; } }
+  if constexpr (NS > 3) { if (ahead >= 2) { wait_vm<PW * 2>(); return; } }
+  if (ahead >= 1) { wait_vm<PW>(); return; }
+  wait_vm<0>();
+}
+
+typedef unsigned long long u64;
+
+// Arrival counters: plain device-scope adds (one round trip, no retries).  A
+// counter is zero when a call starts and the block that uses it last puts it
+// back to zero.
+__device__ inline uint32_t arrive(u64* c, uint32_t k = 1) {
+  return uint32_t(__hip_atomic_fetch_add(c, u64(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+}
+__device__ inline void clear(u64* c) { __hip_atomic_store(c, u64(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+enum Kind { KIND_A = 0, KIND_E = 1, KIND_W = 2 };
+
+// Position of a unit: tile `key` and unit `st` inside it.  A units also carry
+// the adapter slot and the rank tile of the key, expand units the slot and the
+// hi/lo half.  Cursors step one unit at a time, so the loops never divide.
+struct Cur {
+  int key, st, slot, at, hl;
 };
 
-// Stage: DTN rows of the weight side (W or A) from wrow0, then TM rows of X
-// from row 0, K elements [k0, k0 + 64).  Lane l of a group fills row l/8, slot
-// l%8.  Rows past an operand's extent are not fetched.
-template <class G>
-__device__ __forceinline__ void d_issue(char* stage, const i32x4& wres, int wrow0, const i32x4& xres, uint32_t ld,
-                                        int k0, int wave, int lane) {
-  const uint32_t base = lds_addr(stage);
-#pragma unroll
-  for (int i = 0; i < G::PW; ++i) {
-    const int g = wave * G::PW + i;
-    const bool wside = g * 8 < DTN;
-    const int r = g * 8 + (lane >> 3) - (wside ? 0 : DTN);
-    const int c = (lane & 7) ^ ((r >> 1) & 7);
-    const uint32_t off = uint32_t((wside ? wrow0 : 0) + r) * ld + uint32_t(k0 + c * 8) * 2u;
-    dma16(wside ? wres : xres, off, base + uint32_t(g) * 1024u);
-  }
-}
+// One unit's operands: weight-side rows (128, row stride wld) and activation
+// rows (XR, row stride xld), each from byte offset *base.
+struct Unit {
+  i32x4 wres, xres;
+  uint32_t wbase, wld, xbase, xld;
+};
 
-template <int PW, int NS>
-__device__ __forceinline__ void d_wait(int after) {
-  if (NS > 4 && after >= 3) wait_vm<PW * (NS > 4 ? 3 : 0)>();
-  else if (NS > 3 && after >= 2) wait_vm<PW * (NS > 3 ? 2 : 0)>();
-  else if (after >= 1) wait_vm<PW>();
-  else wait_vm<0>();
-}
-
-// Blocks [0, n_used * n_atiles * S) are A tiles, the rest W tiles; block b of
-// a kind takes split b % S of tile b / S.  All four waves load; waves 0 and 1
-// multiply (32 weight rows each, all TM activation rows).
-template <class G>
-__global__ __launch_bounds__(256) void decode_partial_kernel(DecodeArgs d, AdapterTable at) {
-  __shared__ __attribute__((aligned(1024))) char smem[G::NS * G::STAGE];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int na = d.n_used * d.n_atiles * d.S;
-  int b = blockIdx.x;
-  const bool aside = b < na;
-  if (!aside) b -= na;
-  const int s = b % d.S;
-  const int tile = b / d.S;
-  int slot = 0, row0;
-  i32x4 wres;
-  if (aside) {
-    row0 = (tile % d.n_atiles) * DTN;
-    slot = tile / d.n_atiles;
-    wres = make_rsrc_words(at.A[d.slot_adapter[slot]], d.a_bytes);
+__device__ inline Unit unit_of(const Cur& c, Kind kind, const DecodeArgs& d, const AdapterTable& at) {
+  Unit x;
+  if (kind == KIND_E) {
+    x.wres = make_rsrc_words(at.B[d.slot_adapter[c.slot]], d.b_bytes);
+    x.wld = uint32_t(d.rank) * 2u;
+    x.wbase = uint32_t(c.key * TR) * x.wld + uint32_t(c.st) * RB;
+    x.xres = make_rsrc_words(c.hl ? d.TL : d.TH, d.t_bytes);
+    x.xld = x.wld;
+    x.xbase = uint32_t(c.slot * d.M) * x.xld + uint32_t(c.st) * RB;
   } else {
-    row0 = tile * DTN;
-    wres = make_rsrc_words(d.W, d.w_bytes);
-  }
-  const int st0 = s * d.sc, st1 = min(st0 + d.sc, d.nstages);
-  const i32x4 xres = make_rsrc_words(d.X, d.x_bytes);
-  const uint32_t ld = uint32_t(d.K) * 2u;
-  const int nt = st1 - st0;
-
-  // Every tile of a split reads the same K-range of X; starting each tile at a
-  // different stage of its range spreads those reads over many lines at once.
-  const int rot = tile % nt;
-  auto kof = [&](int t) { return (st0 + (t + rot) % nt) * kDecodeStageK; };
-
-  f32x16 acc[G::FM];
-#pragma unroll
-  for (int j = 0; j < G::FM; ++j) acc[j] = f32x16{};
-#pragma unroll
-  for (int p = 0; p < G::NS - 1; ++p)
-    if (p < nt) d_issue<G>(smem + p * G::STAGE, wres, row0, xres, ld, kof(p), wave, lane);
-  for (int t = 0; t < nt; ++t) {
-    d_wait<G::PW, G::NS>(min(G::NS - 2, nt - 1 - t));   // stage t has landed
-    __syncthreads();
-    if (t + G::NS - 1 < nt)             // refill the slot every wave finished reading in stage t-1
-      d_issue<G>(smem + ((t + G::NS - 1) % G::NS) * G::STAGE, wres, row0, xres, ld, kof(t + G::NS - 1), wave,
-                 lane);
-    if (wave < 2) {
-      const char* wt = smem + (t % G::NS) * G::STAGE;
-      const char* xt = wt + DTN * DROW;
-      const int k0 = kof(t);
-#pragma unroll
-      for (int sub = 0; sub < kDecodeStageK / 16; ++sub) {
-        const int c = 2 * sub + (lane >> 5);
-        bf16x8 a = dfrag(wt, wave * 32 + (lane & 31), c);
-        bf16x8 bx[G::FM];
-#pragma unroll
-        for (int j = 0; j < G::FM; ++j) bx[j] = dfrag(xt, j * 32 + (lane & 31), c);
-        if (k0 + kDecodeStageK > d.K && k0 + c * 8 >= d.K) {   // K tail: the first test is uniform
-          a = bf16x8{};
-#pragma unroll
-          for (int j = 0; j < G::FM; ++j) bx[j] = bf16x8{};
-        }
-#pragma unroll
-        for (int j = 0; j < G::FM; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bx[j], acc[j], 0, 0, 0);
-      }
+    x.wld = uint32_t(d.K) * 2u;
+    if (kind == KIND_A) {
+      x.wres = make_rsrc_words(at.A[d.slot_adapter[c.slot]], d.a_bytes);
+      x.wbase = uint32_t(c.at * TR) * x.wld + uint32_t(c.st) * RB;
+    } else {
+      x.wres = make_rsrc_words(d.W, d.w_bytes);
+      x.wbase = uint32_t(c.key * TR) * x.wld + uint32_t(c.st) * RB;
     }
+    x.xres = make_rsrc_words(d.X, d.x_bytes);
+    x.xld = x.wld;
+    x.xbase = uint32_t(c.st) * RB;
   }
-  if (wave >= 2) return;
+  return x;
+}
 
-  // acc[j][q*4+e]: weight row row0 + wave*32 + q*8 + (lane/32)*4 + e, activation row j*32 + lane%32
-  const auto pres = make_rsrc(aside ? static_cast<void*>(d.PT) : static_cast<void*>(d.P),
-                              aside ? d.pt_bytes : d.p_bytes);
-  const int ncols = aside ? d.rank : d.N;
-#pragma unroll
-  for (int j = 0; j < G::FM; ++j) {
-    const int m = j * 32 + (lane & 31);
-    if (m >= d.M) continue;
-    const uint32_t rowbase = aside ? uint32_t((s * d.M + m) * d.n_used + slot) * uint32_t(d.rank)
-                                   : uint32_t(s * d.M + m) * uint32_t(d.N);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int col = row0 + wave * 32 + q * 8 + (lane >> 5) * 4;
-      if (col + 3 < ncols) {
-        const u32x4 v{__float_as_uint(acc[j][q * 4 + 0]), __float_as_uint(acc[j][q * 4 + 1]),
-                      __float_as_uint(acc[j][q * 4 + 2]), __float_as_uint(acc[j][q * 4 + 3])};
-        __builtin_amdgcn_raw_buffer_store_b128(v, pres, (rowbase + uint32_t(col)) * 4u, 0, 0);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-          if (col + e < ncols)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][q * 4 + e]), pres,
-                                                  (rowbase + uint32_t(col + e)) * 4u, 0, 0);
-      }
-    }
+// Spin (thread 0) until the counter reaches `want`; bounded, so a broken
+// hand-over costs time, never a hang.
+__device__ inline void wait_for(u64* c, u64 want) {
+  for (int it = 0; it < (1 << 24); ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return;
+    __builtin_amdgcn_s_sleep(2);
   }
 }
 
-// One thread per four consecutive rank entries of one (adapter slot, row).
-__global__ __launch_bounds__(256) void decode_reduce_kernel(DecodeArgs d) {
-  const int q = blockIdx.x * 256 + threadIdx.x;
-  const int per_row = d.rank / 4;
-  const int total = d.n_used * d.M * per_row;
-  if (q >= total) return;
-  const int jr = (q % per_row) * 4;
-  const int m = (q / per_row) % d.M;
-  const int slot = q / (per_row * d.M);
-  const auto ptres = make_rsrc(d.PT, d.pt_bytes);
-  f32x4 t{0.f, 0.f, 0.f, 0.f};
-  if (d.row_slot[m] == slot) {
-    for (int s0 = 0; s0 < d.S; s0 += 4) {   // four splits in flight, summed in split order
-      f32x4 v[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = s0 + i;
-        const uint32_t off = s < d.S ? ((uint32_t((s * d.M + m) * d.n_used + slot)) * uint32_t(d.rank) +
-                                        uint32_t(jr)) * 4u
-                                     : kMaskedOffset;
-        v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ptres, off, 0, 0));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (s0 + i < d.S) t += v[i];
-    }
-  }
-  float h[4], l[4];
-#pragma unroll
-  for (int e = 0; e < 4; ++e) split_hi_lo(d.scale * t[e], h[e], l[e]);
-  const uint32_t o = (uint32_t(slot * d.M + m) * uint32_t(d.rank) + uint32_t(jr)) * 2u;
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])}, make_rsrc(d.TH, d.t_bytes), o, 0, 0);
-  __builtin_amdgcn_raw_buffer_store_b64(u32x2{pack2(l[0], l[1]), pack2(l[2], l[3])}, make_rsrc(d.TL, d.t_bytes), o, 0, 0);
-}
+template <int MT, bool F32_OUT>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable at) {
+  using G = DG<MT>;
+  __shared__ __attribute__((aligned(1024))) char smem[G::NS * G::STAGE];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t lbase = lds_addr(smem);
 
-// One wave-wide load of 8 rows x 128 bytes (elements [k0, k0 + 64) of rows
-// row0 .. row0+7 of a matrix with row stride ld bytes) into rows lr0 .. lr0+7
-// of a 128-byte-row LDS region, in the swizzled layout.
-__device__ __forceinline__ void dma_rows8(const i32x4& res, int row0, uint32_t ld, int k0, char* region, int lr0,
-                                          int lane) {
-  const int r = lr0 + (lane >> 3);
-  const int c = (lane & 7) ^ ((r >> 1) & 7);
-  const uint32_t off = uint32_t(row0 + (lane >> 3)) * ld + uint32_t(k0 + c * 8) * 2u;
-  dma16(res, off, lds_addr(region + lr0 * DROW));
-}
+  const int nAt = d.n_used * d.ntA;                // A tiles
+  const int nEpt = d.n_used * 2 * d.nrs;           // expand units per W tile
+  const int64_t UE = int64_t(d.ntW) * nEpt;
+  const int64_t UW = int64_t(d.ntW) * d.nst;
+  const int64_t GE = min(int64_t(d.GW), UE);       // W blocks that take expand units (each at least one)
+  u64* const cW = d.cnt;                           // arrivals per W tile
+  u64* const cA = d.cnt + d.ntW;                   // A blocks done
+  u64* const cT = cA + 1;                          // T pieces done
+  u64* const cF = cA + 2;                          // W tiles finished
+  const bool ablock = int(blockIdx.x) < d.GA;
+  const int b = ablock ? int(blockIdx.x) : int(blockIdx.x) - d.GA;
+  const int ka0 = ablock ? int(int64_t(b) * d.nst / d.GA) : 0;        // K units of an A block
+  const int ka1 = ablock ? int(int64_t(b + 1) * d.nst / d.GA) : 0;
 
-// Waves: wn picks 32 of the 64 output columns, wm 64 of the TM rows (FM tiles).
-// All pieces of T and B for up to 256 rank entries arrive by DMA while the W
-// partials are summed, so the block waits on memory about twice in all.
-template <int TM, bool F32_OUT>
-__global__ __launch_bounds__(256) void decode_finish_kernel(DecodeArgs d, AdapterTable at) {
-  constexpr int FMW = TM / 64 > 0 ? (TM / 2) / 32 : 1;    // tiles of 32 rows per wave along m
-  constexpr int PIECE_T = TM * DROW, PIECE_B = DTN * DROW;
-  __shared__ __attribute__((aligned(1024))) char smem[4 * (2 * PIECE_T + PIECE_B)];
-  char* thi = smem;                     // [piece][TM rows][128 B]
-  char* tlo = smem + 4 * PIECE_T;
-  char* bp = smem + 8 * PIECE_T;        // [piece][64 rows][128 B]
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave & 1, wm = wave >> 1;
-  const int n0 = blockIdx.x * DTN;
-  const uint32_t tld = uint32_t(d.rank) * 2u;
-
-  // DMA of the T rows of one adapter slot and of B_a, rank entries [r0, r0 + 64*np)
-  auto fetch = [&](int slot, int r0, int np) {
-    const i32x4 thr = make_rsrc_words(d.TH, d.t_bytes), tlr = make_rsrc_words(d.TL, d.t_bytes);
-    const i32x4 br = make_rsrc_words(at.B[d.slot_adapter[slot]], d.b_bytes);
-    const int tg = TM / 8, groups = np * (2 * tg + DTN / 8);
-    for (int g = wave; g < groups; g += 4) {    // 8-row groups, round-robin over the waves
-      const int piece = g / (2 * tg + DTN / 8), w = g % (2 * tg + DTN / 8);
-      const int k0 = r0 + piece * 64;
-      if (w < tg) dma_rows8(thr, slot * d.M + w * 8, tld, k0, thi + piece * PIECE_T, w * 8, lane);
-      else if (w < 2 * tg) dma_rows8(tlr, slot * d.M + (w - tg) * 8, tld, k0, tlo + piece * PIECE_T, (w - tg) * 8, lane);
-      else dma_rows8(br, n0 + (w - 2 * tg) * 8, tld, k0, bp + piece * PIECE_B, (w - 2 * tg) * 8, lane);
-    }
-  };
-  const bool expand = d.n_used > 0;
-  if (expand) fetch(0, 0, min(4, (d.rank + 63) / 64));
-
-  // acc = sum of the W partials, in split order, four splits in flight
-  f32x16 acc[FMW];
-#pragma unroll
-  for (int j = 0; j < FMW; ++j) acc[j] = f32x16{};
-  const auto pres = make_rsrc(d.P, d.p_bytes);
-  for (int s0 = 0; s0 < d.S; s0 += 4) {
-    f32x4 v[4][FMW][4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < FMW; ++j)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int s = s0 + i, m = wm * (TM / 2) + j * 32 + (lane & 31);
-          const int n = n0 + wn * 32 + q * 8 + (lane >> 5) * 4;
-          const uint32_t off = (s < d.S && m < d.M) ? (uint32_t(s * d.M + m) * uint32_t(d.N) + uint32_t(n)) * 4u
-                                                    : kMaskedOffset;
-          v[i][j][q] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, 0));
-        }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (s0 + i < d.S) {
-#pragma unroll
-        for (int j = 0; j < FMW; ++j)
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[j][q * 4 + e] += v[i][j][q][e];
-      }
-  }
-
-  // expand: acc += T_hi B_a^T + T_lo B_a^T, 256 rank entries per round
-  if (expand) {
-    for (int slot = 0; slot < d.n_used; ++slot) {
-      for (int r0 = 0; r0 < d.rank; r0 += 256) {
-        const int np = min(4, (d.rank - r0 + 63) / 64);
-        if (slot > 0 || r0 > 0) {
-          __syncthreads();             // every wave is done with the previous round's pieces
-          fetch(slot, r0, np);
-        }
-        wait_vm<0>();
-        __syncthreads();
-        for (int piece = 0; piece < np; ++piece) {
-#pragma unroll
-          for (int sub = 0; sub < 4; ++sub) {
-            const int c = 2 * sub + (lane >> 5);
-            bf16x8 a = dfrag(bp + piece * PIECE_B, wn * 32 + (lane & 31), c);
-            const bool past = r0 + piece * 64 + c * 8 >= d.rank;    // rank tail
-            if (past) a = bf16x8{};
-#pragma unroll
-            for (int j = 0; j < FMW; ++j) {
-              const int r = wm * (TM / 2) + j * 32 + (lane & 31);
-              bf16x8 h = dfrag(thi + piece * PIECE_T, r, c), l = dfrag(tlo + piece * PIECE_T, r, c);
-              if (past) h = l = bf16x8{};
-              acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, h, acc[j], 0, 0, 0);
-              acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, l, acc[j], 0, 0, 0);
-            }
+  auto advance = [&](Cur& c, Kind kind) {
+    if (kind == KIND_E) {
+      if (++c.st == d.nrs) {
+        c.st = 0;
+        if (++c.hl == 2) {
+          c.hl = 0;
+          if (++c.slot == d.n_used) {
+            c.slot = 0;
+            ++c.key;
           }
         }
       }
+    } else if (kind == KIND_W) {
+      if (++c.st == d.nst) {
+        c.st = 0;
+        ++c.key;
+      }
+    } else if (++c.st == ka1) {
+      c.st = ka0;
+      ++c.key;
+      if (++c.at == d.ntA) {
+        c.at = 0;
+        ++c.slot;
+      }
     }
-  }
+  };
 
-  // store: acc[j][q*4+e] is column n0 + wn*32 + q*8 + (lane/32)*4 + e of row wm*TM/2 + j*32 + lane%32
-  const auto yres = make_rsrc(d.Y, d.y_bytes);
-  const bool vec = (d.N & 3) == 0;
+  // Weight rows: groups wave + 4 i (i < 4), 8 rows each.  Activation rows:
+  // groups wave + 4 i below 2 MT.  Lane l fills row l / 8, chunk l % 8.
+  auto issue = [&](int slot, const Cur& c, Kind kind) {
+    const Unit x = unit_of(c, kind, d, at);
+    const uint32_t dst = lbase + uint32_t(slot) * G::STAGE;
 #pragma unroll
-  for (int j = 0; j < FMW; ++j) {
-    const int m = wm * (TM / 2) + j * 32 + (lane & 31);
+    for (int i = 0; i < 4; ++i) {
+      const int g = wave + 4 * i;
+      const int r = g * 8 + (lane >> 3);
+      const int ch = (lane & 7) ^ ((r >> 1) & 7);
+      dma16(x.wres, x.wbase + uint32_t(r) * x.wld + uint32_t(ch) * 16u, dst + uint32_t(g) * 1024u);
+    }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int n = n0 + wn * 32 + q * 8 + (lane >> 5) * 4;
-      const uint32_t e0 = uint32_t(m) * uint32_t(d.N) + uint32_t(n);
-      if (vec) {
-        const bool ok = m < d.M && n < d.N;
-        if constexpr (F32_OUT) {
-          const u32x4 w{__float_as_uint(acc[j][q * 4 + 0]), __float_as_uint(acc[j][q * 4 + 1]),
-                        __float_as_uint(acc[j][q * 4 + 2]), __float_as_uint(acc[j][q * 4 + 3])};
-          __builtin_amdgcn_raw_buffer_store_b128(w, yres, ok ? e0 * 4u : kMaskedOffset, 0, 0);
-        } else {
-          const u32x2 w{pack2(acc[j][q * 4 + 0], acc[j][q * 4 + 1]), pack2(acc[j][q * 4 + 2], acc[j][q * 4 + 3])};
-          __builtin_amdgcn_raw_buffer_store_b64(w, yres, ok ? e0 * 2u : kMaskedOffset, 0, 0);
+    for (int i = 0; i < (2 * MT + 3) / 4; ++i) {
+      const int g = wave + 4 * i;
+      if (g < 2 * MT) {
+        const int r = g * 8 + (lane >> 3);
+        const int ch = (lane & 7) ^ ((r >> 1) & 7);
+        const uint32_t off = r < d.M ? x.xbase + uint32_t(r) * x.xld + uint32_t(ch) * 16u : kMaskedOffset;
+        const uint32_t to = dst + uint32_t(TR / 8 + g) * 1024u;
+        if (kind == KIND_E) dma16_dev(x.xres, off, to);   // T, written during this launch
+        else dma16(x.xres, off, to);
+      }
+    }
+  };
+
+  f32x4 acc[2][MT];
+#pragma unroll
+  for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4{};
+
+  // acc[rg][mt][e] is weight row 32 wave + 16 rg + 4 (lane/16) + e of the tile,
+  // activation row 16 mt + lane % 16.  A partial stores acc in that order.
+  auto frag_off = [&](int rg, int mt) { return uint32_t(((wave * 2 + rg) * MT + mt) * 1024 + lane * 16); };
+
+  auto store_partial = [&](float* P, uint32_t pbytes, uint32_t slot) {
+    const auto pres = make_rsrc(P, pbytes);
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rg][mt]), pres,
+                                               slot * uint32_t(G::FRAG) + frag_off(rg, mt), 0, kDeviceScope);
+  };
+
+  // s += partial slots first .. first+n-1, in order, four in flight.
+  auto sum_slots = [&](f32x4 (&s)[2][MT], const float* P, uint32_t pbytes, uint32_t first, int n) {
+    const auto pres = make_rsrc(P, pbytes);
+    for (int j = 0; j < n; j += 4) {
+      f32x4 v[4][2][MT];
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const uint32_t off = j + h < n ? (first + uint32_t(j + h)) * uint32_t(G::FRAG) + frag_off(rg, mt)
+                                           : kMaskedOffset;
+            v[h][rg][mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, kDeviceScope));
+          }
+#pragma unroll
+      for (int h = 0; h < 4; ++h)
+        if (j + h < n) {
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) s[rg][mt] += v[h][rg][mt];
         }
-      } else {
+    }
+  };
+
+  // End of this block's part of W tile `key` (W or expand units).  `verdict`
+  // is a word of the ring slot just consumed, free until the next barrier.
+  auto tile_end = [&](int key, Kind kind, int& verdict) {
+    const int64_t fw = int64_t(key) * d.nst, fe = int64_t(key) * nEpt;
+    const int64_t bw0 = pblock(fw, UW, d.GW);
+    const int nWp = int(pblock(fw + d.nst - 1, UW, d.GW) - bw0 + 1);
+    int nEp = 0;
+    int64_t be0 = 0;
+    if (nEpt > 0) {
+      be0 = pblock(fe, UE, GE);
+      nEp = int(pblock(fe + nEpt - 1, UE, GE) - be0 + 1);
+    }
+    if (kind == KIND_W) store_partial(d.PW, d.pw_bytes, uint32_t(key * d.smaxW + (b - bw0)));
+    else store_partial(d.PE, d.pe_bytes, uint32_t(key * d.smaxE + (b - be0)));
+    wait_vm<0>();          // the partial is out (device scope) before the count
+    __syncthreads();
+    if (tid == 0) verdict = int(arrive(cW + key) + 1 == uint32_t(nWp + nEp));
+    __syncthreads();
+    if (verdict) {
+      f32x4 s[2][MT];
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) s[rg][mt] = f32x4{};
+      sum_slots(s, d.PW, d.pw_bytes, uint32_t(key * d.smaxW), nWp);
+      if (nEp) sum_slots(s, d.PE, d.pe_bytes, uint32_t(key * d.smaxE), nEp);
+      const auto yres = make_rsrc(d.Y, d.y_bytes);
+      const bool vec = (d.N & 3) == 0;
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) {
+          const int m = mt * 16 + (lane & 15);
+          const int n = key * TR + wave * 32 + rg * 16 + 4 * (lane >> 4);
+          const uint32_t e0 = uint32_t(m) * uint32_t(d.N) + uint32_t(n);
+          if (vec) {
+            const bool ok = m < d.M && n < d.N;
+            if constexpr (F32_OUT) {
+              const u32x4 w{__float_as_uint(s[rg][mt][0]), __float_as_uint(s[rg][mt][1]),
+                            __float_as_uint(s[rg][mt][2]), __float_as_uint(s[rg][mt][3])};
+              __builtin_amdgcn_raw_buffer_store_b128(w, yres, ok ? e0 * 4u : kMaskedOffset, 0, 0);
+            } else {
+              const u32x2 w{pack2(s[rg][mt][0], s[rg][mt][1]), pack2(s[rg][mt][2], s[rg][mt][3])};
+              __builtin_amdgcn_raw_buffer_store_b64(w, yres, ok ? e0 * 2u : kMaskedOffset, 0, 0);
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const bool ok = m < d.M && n + e < d.N;
+              if constexpr (F32_OUT)
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(s[rg][mt][e]), yres,
+                                                      ok ? (e0 + e) * 4u : kMaskedOffset, 0, 0);
+              else
+                __builtin_amdgcn_raw_buffer_store_b16(uint16_t(bf16_bits(s[rg][mt][e])), yres,
+                                                      ok ? (e0 + e) * 2u : kMaskedOffset, 0, 0);
+            }
+          }
+        }
+      if (tid == 0) {
+        clear(cW + key);
+        if (arrive(cF) + 1 == uint32_t(d.ntW)) {   // the call is done: T and the A count are no longer read
+          clear(cA);
+          clear(cT);
+          clear(cF);
+        }
+      }
+    }
+#pragma unroll
+    for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4{};
+  };
+
+  // Stream n units of one kind, from cursor c, through the ring.
+  auto run = [&](Cur c, int n, Kind kind) {
+    Cur ci = c;   // next unit to fetch
+    Cur cc = c;   // next unit to multiply
+#pragma unroll
+    for (int p = 0; p < G::NS - 1; ++p)
+      if (p < n) {
+        issue(p, ci, kind);
+        advance(ci, kind);
+      }
+    const int lim = kind == KIND_E ? d.rank : d.K;
+    for (int i = 0; i < n; ++i) {
+      const int ahead = min(G::NS - 2, n - 1 - i);
+      if (wave < G::NA) wait_ring<G::PWA, G::NS>(ahead);
+      else wait_ring<G::PWB, G::NS>(ahead);
+      __syncthreads();
+      if (i + G::NS - 1 < n) {
+        issue((i + G::NS - 1) % G::NS, ci, kind);
+        advance(ci, kind);
+      }
+      const char* ws = smem + (i % G::NS) * G::STAGE;
+      const char* xs = ws + TR * RB;
+      const int e0 = cc.st * UK;
+      const bool tail = lim - e0 < UK;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int ch = 4 * j + (lane >> 4);
+        bf16x8 a[2], bx[MT];
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg) a[rg] = frag(ws, wave * 32 + rg * 16 + (lane & 15), ch);
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt) bx[mt] = frag(xs, mt * 16 + (lane & 15), ch);
+        if (tail && e0 + ch * 8 >= lim) {
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg) a[rg] = bf16x8{};
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) bx[mt] = bf16x8{};
+        }
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            acc[rg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg], bx[mt], acc[rg][mt], 0, 0, 0);
+      }
+      const int key = cc.key;
+      advance(cc, kind);
+      if (i + 1 == n || cc.key != key) {
+        __syncthreads();   // every wave is done with this stage's slot
+        if (kind == KIND_A) {
+          store_partial(d.PA, d.pa_bytes, uint32_t(key * d.GA + b));
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4{};
+        } else {
+          tile_end(key, kind, *reinterpret_cast<int*>(const_cast<char*>(ws)));
+        }
+      }
+    }
+  };
+
+  if (ablock) {
+    // 1. this block's K range of every A tile
+    if (ka1 > ka0) run(Cur{0, ka0, 0, 0, 0}, nAt * (ka1 - ka0), KIND_A);
+    wait_vm<0>();
+    __syncthreads();
+    if (tid == 0) {
+      arrive(cA);
+      wait_for(cA, u64(d.GA));   // every A block has stored its partials
+    }
+    __syncthreads();
+    // 2. T pieces (A tile g, 16-row tile mt), dealt round robin over the A blocks
+    int done = 0;
+    for (int item = b; item < nAt * MT; item += d.GA, ++done) {
+      const int g = item / MT, mt = item % MT, sl = g / d.ntA;
+      const auto pres = make_rsrc(d.PA, d.pa_bytes);
+      f32x4 s[2] = {f32x4{}, f32x4{}};
+      for (int j = 0; j < d.GA; j += 8) {
+        f32x4 v[8][2];
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg) {
+            const uint32_t off = j + h < d.GA ? uint32_t(g * d.GA + j + h) * uint32_t(G::FRAG) + frag_off(rg, mt)
+                                              : kMaskedOffset;
+            v[h][rg] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, kDeviceScope));
+          }
+#pragma unroll
+        for (int h = 0; h < 8; ++h)
+          if (j + h < d.GA) {
+            s[0] += v[h][0];
+            s[1] += v[h][1];
+          }
+      }
+      const auto thr = make_rsrc(d.TH, d.t_bytes), tlr = make_rsrc(d.TL, d.t_bytes);
+      const int m = mt * 16 + (lane & 15);
+      const bool mine = m < d.M && d.row_slot[m] == sl;
+#pragma unroll
+      for (int rg = 0; rg < 2; ++rg) {
+        const int j = (g % d.ntA) * TR + wave * 32 + rg * 16 + 4 * (lane >> 4);
+        const bool ok = m < d.M && j < d.rank;
+        uint32_t hb[4], lb[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const bool ok = m < d.M && n + e < d.N;
-          if constexpr (F32_OUT)
-            __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(acc[j][q * 4 + e]), yres,
-                                                  ok ? (e0 + e) * 4u : kMaskedOffset, 0, 0);
-          else
-            __builtin_amdgcn_raw_buffer_store_b16(uint16_t(bf16_bits(acc[j][q * 4 + e])), yres,
-                                                  ok ? (e0 + e) * 2u : kMaskedOffset, 0, 0);
+          float hi, lo;
+          split_hi_lo(mine ? d.scale * s[rg][e] : 0.0f, hi, lo);
+          hb[e] = bf16_bits(hi);
+          lb[e] = bf16_bits(lo);
         }
+        const uint32_t off = ok ? (uint32_t(sl * d.M + m) * uint32_t(d.rank) + uint32_t(j)) * 2u : kMaskedOffset;
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)}, thr, off, 0,
+                                              kDeviceScope);
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)}, tlr, off, 0,
+                                              kDeviceScope);
+      }
+    }
+    wait_vm<0>();           // T pieces are out before they are counted
+    __syncthreads();
+    if (tid == 0 && done) arrive(cT, uint32_t(done));
+  } else {
+    const int64_t uw0 = pstart(b, UW, d.GW), uw1 = pstart(b + 1, UW, d.GW);
+    if (uw1 > uw0) run(Cur{int(uw0 / d.nst), int(uw0 % d.nst), 0, 0, 0}, int(uw1 - uw0), KIND_W);
+    if (nEpt > 0 && b < GE) {
+      const int64_t ue0 = pstart(b, UE, GE), ue1 = pstart(b + 1, UE, GE);
+      {
+        if (tid == 0) wait_for(cT, u64(nAt * MT));   // all of T is stored
+        __syncthreads();
+        const int r = int(ue0 % nEpt);
+        run(Cur{int(ue0 / nEpt), r % d.nrs, r / (2 * d.nrs), 0, (r / d.nrs) & 1}, int(ue1 - ue0), KIND_E);
       }
     }
   }
 }
 
-using DGeo96 = DGeo<96>;
-using DGeo128 = DGeo<128>;
+template <int MT>
+const void* pick(bool f32_out) {
+  return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true>)
+                 : reinterpret_cast<const void*>(&decode_kernel<MT, false>);
+}
 
 }  // namespace
 
-hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, bool f32_out, hipStream_t stream,
-                         hipEvent_t ev_start, hipEvent_t ev_stop) {
-  DecodeArgs da = d;
-  AdapterTable aa = at;
-  void* args[] = {&da, &aa};
-  const int nblk = (d.n_used * d.n_atiles + d.n_wtiles) * d.S;
-  const void* part = d.M <= 96 ? reinterpret_cast<const void*>(&decode_partial_kernel<DGeo96>)
-                               : reinterpret_cast<const void*>(&decode_partial_kernel<DGeo128>);
-  hipError_t e = hipExtLaunchKernel(part, dim3(nblk), dim3(256), args, 0, stream, ev_start, nullptr, 0);
-  if (e != hipSuccess) return e;
-  if (d.n_used > 0) {
-    void* rargs[] = {&da};
-    const int nr = (d.n_used * d.M * (d.rank / 4) + 255) / 256;
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&decode_reduce_kernel), dim3(nr), dim3(256), rargs, 0, stream);
-    if (e != hipSuccess) return e;
+int decode_mtiles(int64_t M) { return M <= 32 ? 2 : M <= 64 ? 4 : M <= 80 ? 5 : 8; }
+
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used) {
+  DecodePlan p;
+  p.MT = decode_mtiles(M);
+  p.nst = int((K + UK - 1) / UK);
+  p.nrs = int((rank + UK - 1) / UK);
+  p.ntA = int((rank + TR - 1) / TR);
+  p.ntW = int((N + TR - 1) / TR);
+  p.n_used = int(n_used);
+  const int64_t UW = int64_t(p.ntW) * p.nst;
+  // A blocks: enough that one adapter's A units take each of them about 0.6 of
+  // a W block's units, so T is ready well before the W blocks reach the expand.
+  // Planned for one adapter of this rank whatever the batch holds, so the W
+  // split never depends on the adapter rows.
+  const double lw = double(UW) / double(kDecodeBlocks - 16);
+  int ga1 = int(std::ceil(double(p.ntA) * p.nst / (0.6 * lw)));
+  ga1 = std::max(1, std::min({ga1, kDecodeMaxABlocks, p.nst}));
+  p.GW = int(std::min<int64_t>(kDecodeBlocks - ga1, UW));
+  p.GA = n_used > 0 ? ga1 : 0;
+  const int64_t nEpt = n_used * 2 * p.nrs, UE = int64_t(p.ntW) * nEpt;
+  // partial slots per W tile: the most blocks that share one tile
+  p.smaxW = p.smaxE = 0;
+  for (int64_t t = 0; t < p.ntW; ++t) {
+    p.smaxW = std::max<int>(p.smaxW, int(pblock((t + 1) * p.nst - 1, UW, p.GW) - pblock(t * p.nst, UW, p.GW) + 1));
+    if (nEpt > 0)
+      p.smaxE = std::max<int>(p.smaxE, int(pblock((t + 1) * nEpt - 1, UE, std::min<int64_t>(p.GW, UE)) -
+                                           pblock(t * nEpt, UE, std::min<int64_t>(p.GW, UE)) + 1));
   }
-  const void* fin;
-  if (d.M <= 64)
-    fin = f32_out ? reinterpret_cast<const void*>(&decode_finish_kernel<64, true>)
-                  : reinterpret_cast<const void*>(&decode_finish_kernel<64, false>);
-  else
-    fin = f32_out ? reinterpret_cast<const void*>(&decode_finish_kernel<128, true>)
-                  : reinterpret_cast<const void*>(&decode_finish_kernel<128, false>);
-  return hipExtLaunchKernel(fin, dim3(d.n_wtiles), dim3(256), args, 0, stream, nullptr, ev_stop, 0);
+  p.smaxA = p.GA;
+  const size_t frag = size_t(4 * 2 * p.MT * 64 * 16);
+  auto r256 = [](size_t x) { return (x + 255) & ~size_t(255); };
+  p.off_cnt = 0;
+  p.off_pa = LORA_WORKSPACE_COUNTER_BYTES;
+  p.pa_bytes = size_t(n_used * p.ntA) * size_t(p.GA) * frag;
+  p.off_pw = p.off_pa + r256(p.pa_bytes);
+  p.pw_bytes = size_t(p.ntW) * size_t(p.smaxW) * frag;
+  p.off_pe = p.off_pw + r256(p.pw_bytes);
+  p.pe_bytes = size_t(p.ntW) * size_t(p.smaxE) * frag;
+  p.off_th = p.off_pe + r256(p.pe_bytes);
+  p.t_bytes = size_t(n_used) * size_t(M) * size_t(rank) * 2;
+  p.off_tl = p.off_th + r256(p.t_bytes);
+  p.total = p.off_tl + r256(p.t_bytes);
+  return p;
+}
+
+hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
+                         hipEvent_t ev_start, hipEvent_t ev_stop) {
+  const void* k = MT == 2 ? pick<2>(f32_out) : MT == 4 ? pick<4>(f32_out) : MT == 5 ? pick<5>(f32_out)
+                                                                                   : pick<8>(f32_out);
+  DecodeArgs dd = d;
+  AdapterTable aa = at;
+  void* args[] = {&dd, &aa};
+  return hipExtLaunchKernel(k, dim3(unsigned(d.GA + d.GW)), dim3(256), args, 0, stream, ev_start, ev_stop, 0);
 }
 
 }  // namespace lora

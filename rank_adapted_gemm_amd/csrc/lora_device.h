@@ -33,6 +33,18 @@ __device__ __forceinline__ void dma16(const i32x4& res, uint32_t voff, uint32_t 
                "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
 }
 
+// The same load with device-scope coherence (sc1): it reads what other CUs
+// published, past any stale copy in this XCD's L2.
+__device__ __forceinline__ void dma16_dev(const i32x4& res, uint32_t voff, uint32_t lds_addr) {
+  const i32x4 r{__builtin_amdgcn_readfirstlane(res[0]), __builtin_amdgcn_readfirstlane(res[1]),
+                __builtin_amdgcn_readfirstlane(res[2]), __builtin_amdgcn_readfirstlane(res[3])};
+  asm volatile("s_mov_b32 m0, %2\n\tbuffer_load_dwordx4 %0, %1, 0 offen sc1 lds" : : "v"(voff), "s"(r),
+               "s"(__builtin_amdgcn_readfirstlane(lds_addr)) : "memory");
+}
+
+// Cache-policy operand of the buffer load/store builtins: device scope (sc1).
+constexpr int kDeviceScope = 16;
+
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 

@@ -44,44 +44,49 @@ constexpr uint32_t kMaskedOffset = 0x80000000u;
 // Largest M served by the small-M (decode) path.
 constexpr int kDecodeMaxRows = 128;
 
-// Decode path (M <= kDecodeMaxRows).  Three launches:
-//   partial: split-K products of X against 64-row tiles of W (fp32 partials
-//            P[s][m][n]) and of each used adapter's A (partials PT[s][m][slot][j]);
-//   reduce:  T = s * sum_s PT[s] on the rows of each adapter, stored as bf16
-//            hi + lo (zero on other rows);
-//   finish:  Y = sum_s P[s] + T B^T, one store.
-// The split of W over K depends only on (N, K), never on the segment table, so
-// base-only rows come out identical with or without adapter rows beside them.
-constexpr int kDecodeTile = 64;         // rows of W / A per partial tile, columns per finish tile
-constexpr int kDecodeStageK = 64;       // K elements per pipeline stage
-constexpr int kDecodeTargetBlocks = 512;
+// Decode path (M <= kDecodeMaxRows): one launch.  Units are 64-element K slices
+// of 128-row weight tiles.  A blocks (first in the grid) take one K range of
+// every A_a tile each and then reduce T between them; W blocks split the W
+// units evenly and then the expand units (B_a against T); the last block to
+// finish a W tile sums its fp32 partials in block order.
+constexpr int kDecodeTileRows = 128;
+constexpr int kDecodeUnitK = 64;
+constexpr int kDecodeBlocks = 256;      // one block per CU, all resident together
+constexpr int kDecodeMaxABlocks = 32;   // blocks that compute T = s X A^T
 
 struct DecodeArgs {
   const void* X;
   const void* W;
   void* Y;
-  float* P;             // [S][M][N]
-  float* PT;            // [S][M][n_used][rank]
-  uint16_t* TH;         // [n_used][M][rank] bf16 hi part of T
-  uint16_t* TL;         // [n_used][M][rank] bf16 lo part of T
-  uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, p_bytes, pt_bytes, t_bytes;
+  unsigned long long* cnt;   // counter area: arrivals per W tile, A blocks done, T pieces done, W tiles finished
+  float* PA;                 // [A tile][A block] partials, fragment-major
+  float* PW;                 // [W tile][slot]
+  float* PE;                 // [W tile][slot] expand partials
+  uint16_t* TH;              // [n_used][M][rank] bf16 hi part of T
+  uint16_t* TL;              // [n_used][M][rank] bf16 lo part of T
+  uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes, pe_bytes;
   int32_t M, N, K, rank;
   float scale;
-  int32_t nstages;      // ceil(K / kDecodeStageK)
-  int32_t S, sc;        // W splits over K and stages per split
-  int32_t n_wtiles;     // ceil(N / kDecodeTile)
-  int32_t n_atiles;     // ceil(rank / kDecodeTile), per used adapter
-  int32_t n_used;       // adapters named by at least one row
+  int32_t nst;               // units per tile along K: ceil(K / 64)
+  int32_t nrs;               // expand units per tile per half: ceil(rank / 64)
+  int32_t n_used;            // adapters named by at least one row
+  int32_t ntA;               // A tiles per used adapter: ceil(rank / 128)
+  int32_t ntW;               // W tiles: ceil(N / 128)
+  int32_t GA, GW;            // A blocks, W blocks
+  int32_t smaxA, smaxW, smaxE;   // partial slots per tile
   int8_t row_slot[kDecodeMaxRows];           // slot of each row's adapter, -1 for base-only rows
   int8_t slot_adapter[LORA_MAX_ADAPTERS];    // adapter index of each slot
 };
 
-// Split factors of the decode path for a shape.
-struct DecodeSplit {
-  int nstages, S, sc;
+// Grid split and workspace layout of a decode call.  Everything but the
+// adapter work depends on (M, N, K, rank) only.
+struct DecodePlan {
+  int MT;                    // 16-row activation tiles: 2, 4, 5 or 8
+  int nst, nrs, ntA, ntW, n_used;
+  int GA, GW, smaxA, smaxW, smaxE;
+  size_t off_cnt, off_pa, pa_bytes, off_pw, pw_bytes, off_pe, pe_bytes, off_th, t_bytes, off_tl, total;
 };
-DecodeSplit decode_split(int64_t N, int64_t K);
-size_t decode_workspace_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used);
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used);
 
 // Launchers (return the HIP status of the launch).
 hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
@@ -89,7 +94,7 @@ hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const Adapt
 hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
                             bool has_adapter, bool f32_out, bool small_m, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
-hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, bool f32_out, hipStream_t stream,
+hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_f32_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
                              hipStream_t stream);

@@ -48,7 +48,8 @@ def test_one_hip_runtime_in_process():
 def test_limits_match_header():
     text = open(os.path.join(ROOT, "include", "lora_proj.h")).read()
     for name, val in (("LORA_MAX_SEGMENTS", bd.MAX_SEGMENTS), ("LORA_MAX_ADAPTERS", bd.MAX_ADAPTERS),
-                      ("LORA_MIN_RANK", bd.MIN_RANK), ("LORA_MAX_RANK", bd.MAX_RANK)):
+                      ("LORA_MIN_RANK", bd.MIN_RANK), ("LORA_MAX_RANK", bd.MAX_RANK),
+                      ("LORA_WORKSPACE_COUNTER_BYTES", bd.WORKSPACE_COUNTER_BYTES)):
         assert re.search(rf"#define {name} {val}\b", text), name
 
 
@@ -59,16 +60,22 @@ def test_status_strings():
 
 
 def test_workspace_and_path_queries():
-    assert bd.workspace_bytes(16384, 5120, 5120, 256) == 16384 * 256 * 4       # prefill: s X A^T
+    C = bd.WORKSPACE_COUNTER_BYTES
+    assert bd.workspace_bytes(16384, 5120, 5120, 256) == C + 16384 * 256 * 4   # prefill: counters + s X A^T
     assert bd.workspace_bytes(16384, 5120, 5120, 256, 0) == 0                  # prefill, base only
-    assert bd.workspace_bytes(70, 17408, 5120, 256, dtype="f32") == 70 * 256 * 4
+    assert bd.workspace_bytes(70, 17408, 5120, 256, dtype="f32") == C + 70 * 256 * 4
     assert bd.workspace_bytes(64, 512, 250, 16) == 0          # K not a multiple of 8
     assert bd.workspace_bytes(64, 512, 256, 24) == 0          # rank not a multiple of 16
     # decode (<= 128 rows): split-K partials of W always, plus adapter partials
     base = bd.workspace_bytes(70, 5120, 5120, 256, 0)
     one = bd.workspace_bytes(70, 5120, 5120, 256, 1)
     two = bd.workspace_bytes(70, 5120, 5120, 256, 2)
-    assert 0 < base < one < two and base % 256 == 0 and base >= 70 * 5120 * 4
+    assert 0 < base < one < two and base % 256 == 0 and base >= C + 70 * 5120 * 4
+    # decode counters (one per 128 output columns, plus three) must fit the counter area
+    n_fit = (C // 8 - 3) * 128
+    assert bd.path(70, n_fit, 8, 16) == "decode" and bd.workspace_bytes(70, n_fit, 8, 16) > 0
+    assert bd.path(70, n_fit + 128, 8, 16) == "invalid" and bd.workspace_bytes(70, n_fit + 128, 8, 16) == 0
+    assert bd.path(200, n_fit + 128, 8, 16) == "prefill"
     assert bd.path(16384, 5120, 5120, 256) == "prefill"
     assert bd.path(70, 5120, 5120, 256) == "decode"
     assert bd.path(128, 5120, 5120, 256) == "decode"

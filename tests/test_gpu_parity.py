@@ -229,6 +229,31 @@ def test_scale_zero_equals_base():
     assert np.array_equal(a, b)
 
 
+def test_shared_workspace_across_paths_and_shapes():
+    """One zero-filled workspace serves prefill and decode calls of several shapes in a row.
+
+    The prefill path's scratch starts after the counter area, and every decode call leaves its
+    counters at zero, so later calls on the same workspace see a clean counter area.
+    """
+    import torch
+    cases = [synth.random_problem(31, M=300, N=520, K=256, rank=32, seg_starts=[0, 40, 300], seg_adapter=[-1, 0]),
+             synth.random_problem(32, M=70, N=1000, K=520, rank=32, seg_starts=[0, 64, 70], seg_adapter=[0, -1]),
+             synth.random_problem(33, M=9, N=136, K=1032, rank=48, seg_starts=[0, 3, 9], seg_adapter=[-1, 0]),
+             synth.random_problem(34, M=128, N=520, K=256, rank=32, seg_starts=[0, 128], seg_adapter=[0])]
+    need = max(bd.workspace_bytes(p.M, p.N, p.K, p.rank, 1) for p in cases)
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    for rep in range(2):
+        for i, p in enumerate(cases):
+            p.name = f"shared workspace call {rep}.{i} M={p.M} N={p.N} K={p.K}"
+            log(f"case {p.name} path={bd.path(p.M, p.N, p.K, p.rank)}")
+            X, W, A, B = to_device(p)
+            y = bd.lora_proj(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, workspace=ws)
+            torch.cuda.synchronize()
+            check_bf16(p, y, oracle(p))
+            counters = ws[:bd.WORKSPACE_COUNTER_BYTES]
+            assert int(torch.count_nonzero(counters)) == 0, "counter area not back to zero"
+
+
 def test_empty_batch():
     import torch
     X = torch.empty((0, 64), dtype=torch.bfloat16, device="cuda")
