@@ -235,7 +235,6 @@ lora_status lora_proj_ex(const void* X,
     d.cnt = reinterpret_cast<unsigned long long*>(ws + pl.off_cnt);
     d.PA = reinterpret_cast<float*>(ws + pl.off_pa);
     d.PW = reinterpret_cast<float*>(ws + pl.off_pw);
-    d.PE = reinterpret_cast<float*>(ws + pl.off_pe);
     d.TH = reinterpret_cast<uint16_t*>(ws + pl.off_th);
     d.TL = reinterpret_cast<uint16_t*>(ws + pl.off_tl);
     d.x_bytes = uint32_t(x_bytes);
@@ -246,7 +245,6 @@ lora_status lora_proj_ex(const void* X,
     d.t_bytes = uint32_t(pl.t_bytes);
     d.pa_bytes = uint32_t(pl.pa_bytes);
     d.pw_bytes = uint32_t(pl.pw_bytes);
-    d.pe_bytes = uint32_t(pl.pe_bytes);
     d.M = int32_t(M);
     d.N = int32_t(N);
     d.K = int32_t(K);
@@ -259,9 +257,7 @@ lora_status lora_proj_ex(const void* X,
     d.ntW = pl.ntW;
     d.GA = pl.GA;
     d.GW = pl.GW;
-    d.smaxA = pl.smaxA;
     d.smaxW = pl.smaxW;
-    d.smaxE = pl.smaxE;
     for (int g = 0; g < tbl.n; ++g)
       for (int32_t m = tbl.start[g]; m < tbl.start[g + 1]; ++m)
         d.row_slot[m] = tbl.adapter[g] < 0 ? int8_t(-1) : slot_of[tbl.adapter[g]];

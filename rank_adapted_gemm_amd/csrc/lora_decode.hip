@@ -36,6 +36,7 @@
 // block that uses each last, so nothing has to clear them between calls.
 #include <algorithm>
 #include <cmath>
+#include <type_traits>
 
 #include "lora_device.h"
 
@@ -153,9 +154,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 
   const int nAt = d.n_used * d.ntA;                // A tiles
   const int nEpt = d.n_used * 2 * d.nrs;           // expand units per W tile
-  const int64_t UE = int64_t(d.ntW) * nEpt;
   const int64_t UW = int64_t(d.ntW) * d.nst;
-  const int64_t GE = min(int64_t(d.GW), UE);       // W blocks that take expand units (each at least one)
   u64* const cW = d.cnt;                           // arrivals per W tile
   u64* const cA = d.cnt + d.ntW;                   // A blocks done
   u64* const cT = cA + 1;                          // T pieces done
@@ -165,7 +164,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   const int ka0 = ablock ? int(int64_t(b) * d.nst / d.GA) : 0;        // K units of an A block
   const int ka1 = ablock ? int(int64_t(b + 1) * d.nst / d.GA) : 0;
 
-  auto advance = [&](Cur& c, Kind kind) {
+  auto advance = [&](Cur& c, Kind kind) __attribute__((always_inline)) {
     if (kind == KIND_E) {
       if (++c.st == d.nrs) {
         c.st = 0;
@@ -194,7 +193,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 
   // Weight rows: groups wave + 4 i (i < 4), 8 rows each.  Activation rows:
   // groups wave + 4 i below 2 MT.  Lane l fills row l / 8, chunk l % 8.
-  auto issue = [&](int slot, const Cur& c, Kind kind) {
+  auto issue = [&](int slot, const Cur& c, Kind kind) __attribute__((always_inline)) {
     const Unit x = unit_of(c, kind, d, at);
     const uint32_t dst = lbase + uint32_t(slot) * G::STAGE;
 #pragma unroll
@@ -226,9 +225,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 
   // acc[rg][mt][e] is weight row 32 wave + 16 rg + 4 (lane/16) + e of the tile,
   // activation row 16 mt + lane % 16.  A partial stores acc in that order.
-  auto frag_off = [&](int rg, int mt) { return uint32_t(((wave * 2 + rg) * MT + mt) * 1024 + lane * 16); };
+  auto frag_off = [&](int rg, int mt) __attribute__((always_inline)) { return uint32_t(((wave * 2 + rg) * MT + mt) * 1024 + lane * 16); };
 
-  auto store_partial = [&](float* P, uint32_t pbytes, uint32_t slot) {
+  auto store_partial = [&](float* P, uint32_t pbytes, uint32_t slot) __attribute__((always_inline)) {
     const auto pres = make_rsrc(P, pbytes);
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg)
@@ -238,13 +237,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
                                                slot * uint32_t(G::FRAG) + frag_off(rg, mt), 0, kDeviceScope);
   };
 
-  // s += partial slots first .. first+n-1, in order, four in flight.
+  // s += partial slots first .. first+n-1, in order, SB in flight (nothing else
+  // is live when a tile is finished, so the loads may take most registers).
+  constexpr int SB = MT <= 5 ? 8 : 4;
   auto sum_slots = [&](f32x4 (&s)[2][MT], const float* P, uint32_t pbytes, uint32_t first, int n) {
     const auto pres = make_rsrc(P, pbytes);
-    for (int j = 0; j < n; j += 4) {
-      f32x4 v[4][2][MT];
+    for (int j = 0; j < n; j += SB) {
+      f32x4 v[SB][2][MT];
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
+      for (int h = 0; h < SB; ++h)
 #pragma unroll
         for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
             v[h][rg][mt] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, kDeviceScope));
           }
 #pragma unroll
-      for (int h = 0; h < 4; ++h)
+      for (int h = 0; h < SB; ++h)
         if (j + h < n) {
 #pragma unroll
           for (int rg = 0; rg < 2; ++rg)
@@ -264,23 +265,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     }
   };
 
-  // End of this block's part of W tile `key` (W or expand units).  `verdict`
-  // is a word of the ring slot just consumed, free until the next barrier.
-  auto tile_end = [&](int key, Kind kind, int& verdict) {
-    const int64_t fw = int64_t(key) * d.nst, fe = int64_t(key) * nEpt;
+  // End of this block's part of W tile `key` (its W units there, and for its
+  // last tile also its share of the tile's expand units).  `verdict` is a word
+  // of the ring slot just consumed, free until the next barrier.
+  auto tile_end = [&](int key, int& verdict) __attribute__((always_inline)) {
+    const int64_t fw = int64_t(key) * d.nst;
     const int64_t bw0 = pblock(fw, UW, d.GW);
     const int nWp = int(pblock(fw + d.nst - 1, UW, d.GW) - bw0 + 1);
-    int nEp = 0;
-    int64_t be0 = 0;
-    if (nEpt > 0) {
-      be0 = pblock(fe, UE, GE);
-      nEp = int(pblock(fe + nEpt - 1, UE, GE) - be0 + 1);
-    }
-    if (kind == KIND_W) store_partial(d.PW, d.pw_bytes, uint32_t(key * d.smaxW + (b - bw0)));
-    else store_partial(d.PE, d.pe_bytes, uint32_t(key * d.smaxE + (b - be0)));
+    store_partial(d.PW, d.pw_bytes, uint32_t(key * d.smaxW + (b - bw0)));
     wait_vm<0>();          // the partial is out (device scope) before the count
     __syncthreads();
-    if (tid == 0) verdict = int(arrive(cW + key) + 1 == uint32_t(nWp + nEp));
+    if (tid == 0) verdict = int(arrive(cW + key) + 1 == uint32_t(nWp));
     __syncthreads();
     if (verdict) {
       f32x4 s[2][MT];
@@ -289,7 +284,6 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) s[rg][mt] = f32x4{};
       sum_slots(s, d.PW, d.pw_bytes, uint32_t(key * d.smaxW), nWp);
-      if (nEp) sum_slots(s, d.PE, d.pe_bytes, uint32_t(key * d.smaxE), nEp);
       const auto yres = make_rsrc(d.Y, d.y_bytes);
       const bool vec = (d.N & 3) == 0;
 #pragma unroll
@@ -337,29 +331,42 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4{};
   };
 
-  // Stream n units of one kind, from cursor c, through the ring.
-  auto run = [&](Cur c, int n, Kind kind) {
-    Cur ci = c;   // next unit to fetch
-    Cur cc = c;   // next unit to multiply
-#pragma unroll
-    for (int p = 0; p < G::NS - 1; ++p)
-      if (p < n) {
-        issue(p, ci, kind);
-        advance(ci, kind);
+  // Expand units read T: the first of them is fetched only once every T piece
+  // is stored.
+  auto fetch_gate = [&]() __attribute__((always_inline)) {
+    if (tid == 0) wait_for(cT, u64(nAt * MT * 2));
+    __syncthreads();
+  };
+
+  // Stream units through the ring: n0 units of kind K0 from cursor c0, then
+  // n1 expand units from cursor c1 (which continue the tile c0's units end in,
+  // into the same accumulators).  The ring runs on across the change of kind;
+  // each of the two loops multiplies one kind, fixed at compile time.
+  auto run = [&](auto k0c, Cur c0, int n0, Cur c1, int n1) __attribute__((always_inline)) {
+    constexpr Kind K0 = decltype(k0c)::value;
+    const int n = n0 + n1;
+    Cur ci = c0, cc = c0;   // next unit to fetch / to multiply
+    auto fetch = [&](int p) __attribute__((always_inline)) {   // unit p of the sequence into ring slot p % NS
+      if (p < n0) {
+        issue(p % G::NS, ci, K0);
+        if (p + 1 == n0) ci = c1;
+        else advance(ci, K0);
+      } else {
+        if (p == n0) fetch_gate();
+        issue(p % G::NS, ci, KIND_E);
+        advance(ci, KIND_E);
       }
-    const int lim = kind == KIND_E ? d.rank : d.K;
-    for (int i = 0; i < n; ++i) {
+    };
+    auto step = [&](int i, auto kc) __attribute__((always_inline)) {   // multiply unit i (of kind kc)
+      constexpr Kind K = decltype(kc)::value;
       const int ahead = min(G::NS - 2, n - 1 - i);
       if (wave < G::NA) wait_ring<G::PWA, G::NS>(ahead);
       else wait_ring<G::PWB, G::NS>(ahead);
       __syncthreads();
-      if (i + G::NS - 1 < n) {
-        issue((i + G::NS - 1) % G::NS, ci, kind);
-        advance(ci, kind);
-      }
+      if (i + G::NS - 1 < n) fetch(i + G::NS - 1);
       const char* ws = smem + (i % G::NS) * G::STAGE;
       const char* xs = ws + TR * RB;
-      const int e0 = cc.st * UK;
+      const int lim = K == KIND_E ? d.rank : d.K, e0 = cc.st * UK;
       const bool tail = lim - e0 < UK;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -382,25 +389,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
             acc[rg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg], bx[mt], acc[rg][mt], 0, 0, 0);
       }
       const int key = cc.key;
-      advance(cc, kind);
-      if (i + 1 == n || cc.key != key) {
+      if (i + 1 == n0) cc = c1;
+      else advance(cc, K);
+      if (i + 1 == n || (i + 1 < n0 && cc.key != key)) {
         __syncthreads();   // every wave is done with this stage's slot
-        if (kind == KIND_A) {
+        if constexpr (K0 == KIND_A) {
           store_partial(d.PA, d.pa_bytes, uint32_t(key * d.GA + b));
 #pragma unroll
           for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
             for (int mt = 0; mt < MT; ++mt) acc[rg][mt] = f32x4{};
         } else {
-          tile_end(key, kind, *reinterpret_cast<int*>(const_cast<char*>(ws)));
+          tile_end(key, *reinterpret_cast<int*>(const_cast<char*>(ws)));
         }
       }
-    }
+    };
+#pragma unroll
+    for (int p = 0; p < G::NS - 1; ++p)
+      if (p < n) fetch(p);
+    for (int i = 0; i < n0; ++i) step(i, k0c);
+    for (int i = n0; i < n; ++i) step(i, std::integral_constant<Kind, KIND_E>{});
   };
 
   if (ablock) {
     // 1. this block's K range of every A tile
-    if (ka1 > ka0) run(Cur{0, ka0, 0, 0, 0}, nAt * (ka1 - ka0), KIND_A);
+    if (ka1 > ka0)
+      run(std::integral_constant<Kind, KIND_A>{}, Cur{0, ka0, 0, 0, 0}, nAt * (ka1 - ka0), Cur{0, 0, 0, 0, 0}, 0);
     wait_vm<0>();
     __syncthreads();
     if (tid == 0) {
@@ -408,66 +422,63 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       wait_for(cA, u64(d.GA));   // every A block has stored its partials
     }
     __syncthreads();
-    // 2. T pieces (A tile g, 16-row tile mt), dealt round robin over the A blocks
+    // 2. T pieces (A tile g, 16-row tile mt, 16-column group rg), dealt round
+    //    robin over the A blocks; each wave sums its own fragments of every A
+    //    block's partial, all loads in flight at once.
     int done = 0;
-    for (int item = b; item < nAt * MT; item += d.GA, ++done) {
-      const int g = item / MT, mt = item % MT, sl = g / d.ntA;
+    for (int item = b; item < nAt * MT * 2; item += d.GA, ++done) {
+      const int g = item / (MT * 2), mt = (item / 2) % MT, rg = item & 1, sl = g / d.ntA;
       const auto pres = make_rsrc(d.PA, d.pa_bytes);
-      f32x4 s[2] = {f32x4{}, f32x4{}};
-      for (int j = 0; j < d.GA; j += 8) {
-        f32x4 v[8][2];
+      f32x4 v[kDecodeMaxABlocks];
 #pragma unroll
-        for (int h = 0; h < 8; ++h)
-#pragma unroll
-          for (int rg = 0; rg < 2; ++rg) {
-            const uint32_t off = j + h < d.GA ? uint32_t(g * d.GA + j + h) * uint32_t(G::FRAG) + frag_off(rg, mt)
-                                              : kMaskedOffset;
-            v[h][rg] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, kDeviceScope));
-          }
-#pragma unroll
-        for (int h = 0; h < 8; ++h)
-          if (j + h < d.GA) {
-            s[0] += v[h][0];
-            s[1] += v[h][1];
-          }
+      for (int h = 0; h < kDecodeMaxABlocks; ++h) {
+        const uint32_t off = h < d.GA ? uint32_t(g * d.GA + h) * uint32_t(G::FRAG) + frag_off(rg, mt) : kMaskedOffset;
+        v[h] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, off, 0, kDeviceScope));
       }
+      f32x4 sum = f32x4{};
+#pragma unroll
+      for (int h = 0; h < kDecodeMaxABlocks; ++h)
+        if (h < d.GA) sum += v[h];
       const auto thr = make_rsrc(d.TH, d.t_bytes), tlr = make_rsrc(d.TL, d.t_bytes);
       const int m = mt * 16 + (lane & 15);
       const bool mine = m < d.M && d.row_slot[m] == sl;
+      const int j = (g % d.ntA) * TR + wave * 32 + rg * 16 + 4 * (lane >> 4);
+      const bool ok = m < d.M && j < d.rank;
+      uint32_t hb[4], lb[4];
 #pragma unroll
-      for (int rg = 0; rg < 2; ++rg) {
-        const int j = (g % d.ntA) * TR + wave * 32 + rg * 16 + 4 * (lane >> 4);
-        const bool ok = m < d.M && j < d.rank;
-        uint32_t hb[4], lb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float hi, lo;
-          split_hi_lo(mine ? d.scale * s[rg][e] : 0.0f, hi, lo);
-          hb[e] = bf16_bits(hi);
-          lb[e] = bf16_bits(lo);
-        }
-        const uint32_t off = ok ? (uint32_t(sl * d.M + m) * uint32_t(d.rank) + uint32_t(j)) * 2u : kMaskedOffset;
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)}, thr, off, 0,
-                                              kDeviceScope);
-        __builtin_amdgcn_raw_buffer_store_b64(u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)}, tlr, off, 0,
-                                              kDeviceScope);
+      for (int e = 0; e < 4; ++e) {
+        float hi, lo;
+        split_hi_lo(mine ? d.scale * sum[e] : 0.0f, hi, lo);
+        hb[e] = bf16_bits(hi);
+        lb[e] = bf16_bits(lo);
       }
+      const uint32_t off = ok ? (uint32_t(sl * d.M + m) * uint32_t(d.rank) + uint32_t(j)) * 2u : kMaskedOffset;
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)}, thr, off, 0,
+                                            kDeviceScope);
+      __builtin_amdgcn_raw_buffer_store_b64(u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)}, tlr, off, 0,
+                                            kDeviceScope);
     }
     wait_vm<0>();           // T pieces are out before they are counted
     __syncthreads();
     if (tid == 0 && done) arrive(cT, uint32_t(done));
   } else {
     const int64_t uw0 = pstart(b, UW, d.GW), uw1 = pstart(b + 1, UW, d.GW);
-    if (uw1 > uw0) run(Cur{int(uw0 / d.nst), int(uw0 % d.nst), 0, 0, 0}, int(uw1 - uw0), KIND_W);
-    if (nEpt > 0 && b < GE) {
-      const int64_t ue0 = pstart(b, UE, GE), ue1 = pstart(b + 1, UE, GE);
-      {
-        if (tid == 0) wait_for(cT, u64(nAt * MT));   // all of T is stored
-        __syncthreads();
-        const int r = int(ue0 % nEpt);
-        run(Cur{int(ue0 / nEpt), r % d.nrs, r / (2 * d.nrs), 0, (r / d.nrs) & 1}, int(ue1 - ue0), KIND_E);
-      }
+    const int nw = int(uw1 - uw0);
+    // expand units of the tile this block's W units end in, split evenly
+    // over the blocks whose W units end in that tile
+    int ne = 0;
+    Cur ce{0, 0, 0, 0, 0};
+    if (nEpt > 0 && nw > 0) {
+      const int t = int((uw1 - 1) / d.nst);
+      const int64_t e_lo = pblock(int64_t(t) * d.nst, UW, d.GW);
+      const int64_t bb = pblock(int64_t(t + 1) * d.nst - 1, UW, d.GW);
+      const int64_t e_hi = pstart(bb + 1, UW, d.GW) == int64_t(t + 1) * d.nst ? bb : bb - 1;
+      const int n_end = int(e_hi - e_lo + 1), idx = int(b - e_lo);
+      const int r0 = idx * nEpt / n_end, r1 = (idx + 1) * nEpt / n_end;
+      ne = r1 - r0;
+      ce = Cur{t, r0 % d.nrs, r0 / (2 * d.nrs), 0, (r0 / d.nrs) & 1};
     }
+    if (nw > 0) run(std::integral_constant<Kind, KIND_W>{}, Cur{int(uw0 / d.nst), int(uw0 % d.nst), 0, 0, 0}, nw, ce, ne);
   }
 }
 
@@ -490,25 +501,23 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_
   p.ntW = int((N + TR - 1) / TR);
   p.n_used = int(n_used);
   const int64_t UW = int64_t(p.ntW) * p.nst;
-  // A blocks: enough that one adapter's A units take each of them about 0.6 of
-  // a W block's units, so T is ready well before the W blocks reach the expand.
-  // Planned for one adapter of this rank whatever the batch holds, so the W
-  // split never depends on the adapter rows.
+  // A blocks: enough that one adapter's A units take each of them about 0.35
+  // of a W block's units, so T is ready well before the W blocks reach the
+  // expand (the A blocks also meet and reduce T after their units).  Planned
+  // for one adapter of this rank whatever the batch holds, so the W split
+  // never depends on the adapter rows.
   const double lw = double(UW) / double(kDecodeBlocks - 16);
-  int ga1 = int(std::ceil(double(p.ntA) * p.nst / (0.6 * lw)));
+  int ga1 = int(std::ceil(double(p.ntA) * p.nst / (0.35 * lw)));
   ga1 = std::max(1, std::min({ga1, kDecodeMaxABlocks, p.nst}));
+  // W blocks: the rest of the CUs, but at least one per W tile, so that the W
+  // units of every tile end in some block (which takes the tile's expand units).
   p.GW = int(std::min<int64_t>(kDecodeBlocks - ga1, UW));
+  p.GW = std::max(p.GW, p.ntW);
   p.GA = n_used > 0 ? ga1 : 0;
-  const int64_t nEpt = n_used * 2 * p.nrs, UE = int64_t(p.ntW) * nEpt;
   // partial slots per W tile: the most blocks that share one tile
-  p.smaxW = p.smaxE = 0;
-  for (int64_t t = 0; t < p.ntW; ++t) {
+  p.smaxW = 0;
+  for (int64_t t = 0; t < p.ntW; ++t)
     p.smaxW = std::max<int>(p.smaxW, int(pblock((t + 1) * p.nst - 1, UW, p.GW) - pblock(t * p.nst, UW, p.GW) + 1));
-    if (nEpt > 0)
-      p.smaxE = std::max<int>(p.smaxE, int(pblock((t + 1) * nEpt - 1, UE, std::min<int64_t>(p.GW, UE)) -
-                                           pblock(t * nEpt, UE, std::min<int64_t>(p.GW, UE)) + 1));
-  }
-  p.smaxA = p.GA;
   const size_t frag = size_t(4 * 2 * p.MT * 64 * 16);
   auto r256 = [](size_t x) { return (x + 255) & ~size_t(255); };
   p.off_cnt = 0;
@@ -516,9 +525,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_
   p.pa_bytes = size_t(n_used * p.ntA) * size_t(p.GA) * frag;
   p.off_pw = p.off_pa + r256(p.pa_bytes);
   p.pw_bytes = size_t(p.ntW) * size_t(p.smaxW) * frag;
-  p.off_pe = p.off_pw + r256(p.pw_bytes);
-  p.pe_bytes = size_t(p.ntW) * size_t(p.smaxE) * frag;
-  p.off_th = p.off_pe + r256(p.pe_bytes);
+  p.off_th = p.off_pw + r256(p.pw_bytes);
   p.t_bytes = size_t(n_used) * size_t(M) * size_t(rank) * 2;
   p.off_tl = p.off_th + r256(p.t_bytes);
   p.total = p.off_tl + r256(p.t_bytes);

@@ -47,8 +47,9 @@ constexpr int kDecodeMaxRows = 128;
 // Decode path (M <= kDecodeMaxRows): one launch.  Units are 64-element K slices
 // of 128-row weight tiles.  A blocks (first in the grid) take one K range of
 // every A_a tile each and then reduce T between them; W blocks split the W
-// units evenly and then the expand units (B_a against T); the last block to
-// finish a W tile sums its fp32 partials in block order.
+// units evenly, each followed by its share of the expand units (B_a against T)
+// of the tile its W units end in; the last block to finish a W tile sums the
+// tile's fp32 partials in block order.
 constexpr int kDecodeTileRows = 128;
 constexpr int kDecodeUnitK = 64;
 constexpr int kDecodeBlocks = 256;      // one block per CU, all resident together
@@ -61,10 +62,9 @@ struct DecodeArgs {
   unsigned long long* cnt;   // counter area: arrivals per W tile, A blocks done, T pieces done, W tiles finished
   float* PA;                 // [A tile][A block] partials, fragment-major
   float* PW;                 // [W tile][slot]
-  float* PE;                 // [W tile][slot] expand partials
   uint16_t* TH;              // [n_used][M][rank] bf16 hi part of T
   uint16_t* TL;              // [n_used][M][rank] bf16 lo part of T
-  uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes, pe_bytes;
+  uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes;
   int32_t M, N, K, rank;
   float scale;
   int32_t nst;               // units per tile along K: ceil(K / 64)
@@ -73,7 +73,7 @@ struct DecodeArgs {
   int32_t ntA;               // A tiles per used adapter: ceil(rank / 128)
   int32_t ntW;               // W tiles: ceil(N / 128)
   int32_t GA, GW;            // A blocks, W blocks
-  int32_t smaxA, smaxW, smaxE;   // partial slots per tile
+  int32_t smaxW;             // partial slots per W tile
   int8_t row_slot[kDecodeMaxRows];           // slot of each row's adapter, -1 for base-only rows
   int8_t slot_adapter[LORA_MAX_ADAPTERS];    // adapter index of each slot
 };
@@ -83,8 +83,8 @@ struct DecodeArgs {
 struct DecodePlan {
   int MT;                    // 16-row activation tiles: 2, 4, 5 or 8
   int nst, nrs, ntA, ntW, n_used;
-  int GA, GW, smaxA, smaxW, smaxE;
-  size_t off_cnt, off_pa, pa_bytes, off_pw, pw_bytes, off_pe, pe_bytes, off_th, t_bytes, off_tl, total;
+  int GA, GW, smaxW;
+  size_t off_cnt, off_pa, pa_bytes, off_pw, pw_bytes, off_th, t_bytes, off_tl, total;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used);
 
