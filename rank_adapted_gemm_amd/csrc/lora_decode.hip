@@ -15,13 +15,15 @@
 //     (tile, 16-row) pieces, and store it as bf16 hi = bf16(T), lo =
 //     bf16(T - hi), zero on rows that name another adapter or none.
 //   * W blocks (one per remaining CU) split the W units evenly and in order
-//     (stream-K), then their share of the expand units: B_a's rows against
-//     T_hi and T_lo.  By then T is normally done; if not, they wait for it.
+//     (stream-K).  The expand units of a tile (B_a's rows against T_hi and
+//     T_lo) are shared out among the blocks whose W range ends in that tile,
+//     and each adds its share into the same accumulators as its last W units,
+//     so a tile has one partial per block and no separate expand partials.
+//     The first expand unit waits for T if the A blocks are not done yet.
 //   * At the end of its part of a W tile a block stores its fp32 partial
 //     (fragment-major, so stores and reloads are whole 1 KiB lines) and counts
-//     itself in on the tile.  The last one in sums the tile's W partials and
-//     then its expand partials, in block order (so the result does not depend
-//     on timing), and stores Y once.
+//     itself in on the tile.  The last one in sums the tile's partials in
+//     block order (so the result does not depend on timing) and stores Y once.
 //
 // The split of the W units depends on (N, K, r) only, and the expand adds exact
 // zeros on rows that name no adapter, so base-only rows come out bitwise the
