@@ -74,18 +74,28 @@ __device__ __forceinline__ void wait_stages(int stages) {
   else wait_vm<0>();
 }
 
+// A wave's PW loads of a stage are consecutive 16-row groups of one side (the
+// weight rows come first and fill whole waves), so they go out in groups of up
+// to four under one M0 value.
 template <class C>
 __device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane) {
+  static_assert((C::TN / 16) % C::PW == 0, "a wave's groups must lie on one side");
+  constexpr int NG = C::PW < 4 ? C::PW : 4;
+  static_assert(C::PW % NG == 0, "groups of loads must split evenly");
   const uint32_t base = lds_addr(stage);
+  const int g0 = wave * C::PW;                      // first 16-row group of the wave (uniform)
+  const bool wside = g0 * 16 < C::TN;
+  const Side& sd = wside ? ws : xs;
 #pragma unroll
-  for (int i = 0; i < C::PW; ++i) {
-    const int g = wave * C::PW + i;                 // 16-row group of the stage (uniform)
-    const bool wside = g * 16 < C::TN;
-    const Side& sd = wside ? ws : xs;
-    const int r = g * 16 + (lane >> 2) - (wside ? 0 : C::TN);
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
-    const uint32_t off = uint32_t(sd.row0 + r) * sd.ld_bytes + uint32_t(k0 + c * 8) * 2u;
-    dma16(sd.res, off, base + uint32_t(g) * 1024u);
+  for (int q = 0; q < C::PW; q += NG) {
+    uint32_t off[NG];
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const int r = (g0 + q + i) * 16 + (lane >> 2) - (wside ? 0 : C::TN);
+      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      off[i] = uint32_t(sd.row0 + r) * sd.ld_bytes + uint32_t(k0 + c * 8) * 2u;
+    }
+    dma16_group<NG>(sd.res, off, base + uint32_t(g0 + q) * 1024u);
   }
 }
 

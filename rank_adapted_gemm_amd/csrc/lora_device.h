@@ -45,6 +45,76 @@ __device__ __forceinline__ void dma16_dev(const i32x4& res, uint32_t voff, uint3
 // Cache-policy operand of the buffer load/store builtins: device scope (sc1).
 constexpr int kDeviceScope = 16;
 
+// Offset for a masked lane of dma16_group: past the end of every operand even
+// after subtracting the group's instruction offsets (at most 3 KiB).
+constexpr uint32_t kDmaMaskedOffset = 0xFFFFF000u;
+
+// Up to four wave-wide 16-byte global -> LDS loads under one M0 value: load i
+// reads voff[i] and lands at lds_addr + 1024 * i.  The instruction offset
+// (i KiB) moves the LDS destination and the memory address alike, so voff[i]
+// is biased down by the same amount.  Rewriting M0 before every LDS-DMA load
+// holds the wave until the previous one has left; a wave that writes M0 once
+// per group of four moves about 2.6 times as many bytes.  Masked lanes pass
+// kDmaMaskedOffset.  SC1 selects device-scope (sc1) loads.
+template <int NL, bool SC1 = false>
+__device__ __forceinline__ void dma16_group(const i32x4& res, const uint32_t (&voff)[NL], uint32_t lds_addr) {
+  static_assert(NL >= 1 && NL <= 4, "one M0 covers at most four 1 KiB blocks (instruction offset < 4 KiB)");
+  const i32x4 r{__builtin_amdgcn_readfirstlane(res[0]), __builtin_amdgcn_readfirstlane(res[1]),
+                __builtin_amdgcn_readfirstlane(res[2]), __builtin_amdgcn_readfirstlane(res[3])};
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  const uint32_t v0 = voff[0];
+  const uint32_t v1 = NL > 1 ? voff[NL > 1 ? 1 : 0] - 1024u : 0u;
+  const uint32_t v2 = NL > 2 ? voff[NL > 2 ? 2 : 0] - 2048u : 0u;
+  const uint32_t v3 = NL > 3 ? voff[NL > 3 ? 3 : 0] - 3072u : 0u;
+  if constexpr (NL == 1) {
+    if constexpr (SC1)
+      asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen sc1 lds" : : "v"(v0), "s"(m0), "s"(r)
+                   : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %1\n\tbuffer_load_dwordx4 %0, %2, 0 offen lds" : : "v"(v0), "s"(m0), "s"(r)
+                   : "memory");
+  } else if constexpr (NL == 2) {
+    if constexpr (SC1)
+      asm volatile("s_mov_b32 m0, %2\n\t"
+                   "buffer_load_dwordx4 %0, %3, 0 offen sc1 lds\n\t"
+                   "buffer_load_dwordx4 %1, %3, 0 offen offset:1024 sc1 lds"
+                   : : "v"(v0), "v"(v1), "s"(m0), "s"(r) : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %2\n\t"
+                   "buffer_load_dwordx4 %0, %3, 0 offen lds\n\t"
+                   "buffer_load_dwordx4 %1, %3, 0 offen offset:1024 lds"
+                   : : "v"(v0), "v"(v1), "s"(m0), "s"(r) : "memory");
+  } else if constexpr (NL == 3) {
+    if constexpr (SC1)
+      asm volatile("s_mov_b32 m0, %3\n\t"
+                   "buffer_load_dwordx4 %0, %4, 0 offen sc1 lds\n\t"
+                   "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 sc1 lds\n\t"
+                   "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 sc1 lds"
+                   : : "v"(v0), "v"(v1), "v"(v2), "s"(m0), "s"(r) : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %3\n\t"
+                   "buffer_load_dwordx4 %0, %4, 0 offen lds\n\t"
+                   "buffer_load_dwordx4 %1, %4, 0 offen offset:1024 lds\n\t"
+                   "buffer_load_dwordx4 %2, %4, 0 offen offset:2048 lds"
+                   : : "v"(v0), "v"(v1), "v"(v2), "s"(m0), "s"(r) : "memory");
+  } else {
+    if constexpr (SC1)
+      asm volatile("s_mov_b32 m0, %4\n\t"
+                   "buffer_load_dwordx4 %0, %5, 0 offen sc1 lds\n\t"
+                   "buffer_load_dwordx4 %1, %5, 0 offen offset:1024 sc1 lds\n\t"
+                   "buffer_load_dwordx4 %2, %5, 0 offen offset:2048 sc1 lds\n\t"
+                   "buffer_load_dwordx4 %3, %5, 0 offen offset:3072 sc1 lds"
+                   : : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(m0), "s"(r) : "memory");
+    else
+      asm volatile("s_mov_b32 m0, %4\n\t"
+                   "buffer_load_dwordx4 %0, %5, 0 offen lds\n\t"
+                   "buffer_load_dwordx4 %1, %5, 0 offen offset:1024 lds\n\t"
+                   "buffer_load_dwordx4 %2, %5, 0 offen offset:2048 lds\n\t"
+                   "buffer_load_dwordx4 %3, %5, 0 offen offset:3072 lds"
+                   : : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(m0), "s"(r) : "memory");
+  }
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 
