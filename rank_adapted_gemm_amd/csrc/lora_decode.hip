@@ -193,29 +193,44 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     }
   };
 
-  // Weight rows: groups wave + 4 i (i < 4), 8 rows each.  Activation rows:
-  // groups wave + 4 i below 2 MT.  Lane l fills row l / 8, chunk l % 8.
+  // Weight rows: wave w loads 8-row groups 4w .. 4w+3.  Activation rows: the
+  // 2 MT groups are dealt out in consecutive runs, one more to each of the
+  // first (2 MT) % 4 waves.  Lane l fills row l / 8, chunk l % 8.  Each run
+  // goes out under one M0 value.
+  constexpr int XG = 2 * MT, XQ = XG / 4, XREM = XG % 4;
+  const int xcount = XQ + (wave < XREM ? 1 : 0);
+  const int xfirst = wave * XQ + min(wave, XREM);
   auto issue = [&](int slot, const Cur& c, Kind kind) __attribute__((always_inline)) {
     const Unit x = unit_of(c, kind, d, at);
     const uint32_t dst = lbase + uint32_t(slot) * G::STAGE;
+    {
+      uint32_t off[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = wave + 4 * i;
-      const int r = g * 8 + (lane >> 3);
-      const int ch = (lane & 7) ^ ((r >> 1) & 7);
-      dma16(x.wres, x.wbase + uint32_t(r) * x.wld + uint32_t(ch) * 16u, dst + uint32_t(g) * 1024u);
-    }
-#pragma unroll
-    for (int i = 0; i < (2 * MT + 3) / 4; ++i) {
-      const int g = wave + 4 * i;
-      if (g < 2 * MT) {
-        const int r = g * 8 + (lane >> 3);
+      for (int i = 0; i < 4; ++i) {
+        const int r = (4 * wave + i) * 8 + (lane >> 3);
         const int ch = (lane & 7) ^ ((r >> 1) & 7);
-        const uint32_t off = r < d.M ? x.xbase + uint32_t(r) * x.xld + uint32_t(ch) * 16u : kMaskedOffset;
-        const uint32_t to = dst + uint32_t(TR / 8 + g) * 1024u;
-        if (kind == KIND_E) dma16_dev(x.xres, off, to);   // T, written during this launch
-        else dma16(x.xres, off, to);
+        off[i] = x.wbase + uint32_t(r) * x.wld + uint32_t(ch) * 16u;
       }
+      dma16_group<4>(x.wres, off, dst + uint32_t(4 * wave) * 1024u);
+    }
+    auto xrun = [&](auto nc) __attribute__((always_inline)) {
+      constexpr int NL = decltype(nc)::value;
+      uint32_t off[NL];
+#pragma unroll
+      for (int i = 0; i < NL; ++i) {
+        const int r = (xfirst + i) * 8 + (lane >> 3);
+        const int ch = (lane & 7) ^ ((r >> 1) & 7);
+        off[i] = r < d.M ? x.xbase + uint32_t(r) * x.xld + uint32_t(ch) * 16u : kDmaMaskedOffset;
+      }
+      const uint32_t to = dst + uint32_t(TR / 8 + xfirst) * 1024u;
+      if (kind == KIND_E) dma16_group<NL, true>(x.xres, off, to);   // T, written during this launch
+      else dma16_group<NL>(x.xres, off, to);
+    };
+    if constexpr (XREM == 0) {
+      xrun(std::integral_constant<int, XQ>{});
+    } else {
+      if (xcount == XQ + 1) xrun(std::integral_constant<int, XQ + 1>{});
+      else xrun(std::integral_constant<int, XQ>{});
     }
   };
 
