@@ -140,6 +140,38 @@ lora_status lora_proj_ex(const void* X,
                          hipStream_t stream,
                          hipEvent_t main_start, hipEvent_t main_stop);
 
+/*
+ * lora_proj_multi — lora_proj with one scale per adapter.
+ *
+ * Several adapters serve one batch ("two 27B models on a single RTX 5090",
+ * section 4 request-path figure: each request names its model, and requests
+ * naming different models share the batch).  Rows of a segment naming adapter
+ * a get
+ *
+ *     Y[m,:] = X[m,:] W^T + scales[a] (X[m,:] A_a^T) B_a^T
+ *
+ * and base-only rows get X[m,:] W^T, exactly as in lora_proj.  Arguments,
+ * checks, workspace and results are lora_proj's, with
+ *
+ *   scales       HOST array of n_adapters floats (may be released on return);
+ *                NULL with n_adapters > 0 returns LORA_EINVAL
+ *
+ * in place of the single `scale`.  All adapters of one call share `rank`.  An
+ * adapter of smaller rank r_a is passed zero-padded to `rank` (A_a rows and B_a
+ * columns r_a .. rank-1 zero): the padded terms add exact zeros, so the result
+ * equals the one at rank r_a to the last bit.
+ */
+lora_status lora_proj_multi(const void* X,
+                            const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                            const void* W,
+                            const void* const* A, const void* const* B,
+                            int32_t n_adapters, int32_t rank, const float* scales,
+                            void* Y,
+                            int64_t M, int64_t N, int64_t K,
+                            lora_dtype dtype,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
 /* Workspace bytes lora_proj needs for any segment table of this shape that names at most
  * n_adapters adapters (an upper bound), counter area included.  Returns 0 for invalid
  * arguments.  Batches of at most 128 rows (the decode path) always need a workspace, for its

@@ -9,10 +9,11 @@ Source: "two 27B models on a single RTX 5090" (blog.kvit.app).
     thin matrices applied in turn; a request that names the base model uses the
     base weights alone; both kinds of request share one batch.
 
-So, for a token row x of a request naming adapter a (s is the call's scale,
-1.0 for the pages' unscaled merge):
+So, for a token row x of a request naming adapter a (s_a is that adapter's
+scale, 1.0 for the pages' unscaled merge; a call may give one s for every
+adapter or one per adapter, since each adapter is its own merge):
 
-    y = x W^T + s * ((x A_a^T) B_a^T)
+    y = x W^T + s_a * ((x A_a^T) B_a^T)
 
 and for every other row y = x W^T.  The rows of one request are contiguous:
 segment g covers rows [seg_starts[g], seg_starts[g+1]) and seg_adapter[g] is
@@ -47,11 +48,13 @@ def validate_segments(seg_starts, seg_adapter, M: int, n_adapters: int):
 
 
 def lora_proj_ref(X, seg_starts, seg_adapter, W, A, B, scale, rows=None) -> np.ndarray:
-    """Y = X W^T, plus s (X A_a^T) B_a^T on the rows of segments naming adapter a.
+    """Y = X W^T, plus s_a (X A_a^T) B_a^T on the rows of segments naming adapter a.
 
-    X: (M, K), W: (N, K), A: list of (r, K), B: list of (N, r) — exact input
-    values (any float dtype).  rows: optional global row indices; only those
-    rows of Y are computed (rows are independent of one another).
+    X: (M, K), W: (N, K), A: list of (r_a, K), B: list of (N, r_a) — exact
+    input values (any float dtype); each adapter may have its own rank r_a.
+    scale: one number for every adapter, or a sequence with one per adapter.
+    rows: optional global row indices; only those rows of Y are computed (rows
+    are independent of one another).
     Returns float64 of shape (len(rows), N).
     """
     X = np.asarray(X)
@@ -61,6 +64,12 @@ def lora_proj_ref(X, seg_starts, seg_adapter, W, A, B, scale, rows=None) -> np.n
     if W64.shape[1] != K:
         raise ValueError("W must be N x K")
     s, a = validate_segments(seg_starts, seg_adapter, M, len(A))
+    if np.ndim(scale) == 0:
+        scales = [float(scale)] * len(A)
+    else:
+        scales = [float(v) for v in scale]
+        if len(scales) != len(A):
+            raise ValueError("one scale per adapter")
     rows = np.arange(M, dtype=np.int64) if rows is None else np.asarray(rows, dtype=np.int64)
     Y = np.empty((len(rows), N), dtype=np.float64)
     if len(rows) == 0:
@@ -79,5 +88,5 @@ def lora_proj_ref(X, seg_starts, seg_adapter, W, A, B, scale, rows=None) -> np.n
         if A64.shape[1] != K or B64.shape[0] != N or A64.shape[0] != B64.shape[1]:
             raise ValueError("A must be r x K and B must be N x r")
         t = x @ A64.T                  # the first thin matrix: r values per row
-        Y[pos] = base + float(scale) * (t @ B64.T)   # the second, added to the base
+        Y[pos] = base + scales[adapter] * (t @ B64.T)   # the second, added to the base
     return Y

@@ -8,6 +8,7 @@ is no other path.
 from __future__ import annotations
 
 import ctypes
+import numbers
 import os
 
 PKG = os.path.dirname(os.path.abspath(__file__))
@@ -19,7 +20,8 @@ STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESEGMENTS", 3: "LORA_EA
 DTYPES = {"bf16": 0, "f32": 1, "bf16_f32out": 2}
 MAX_SEGMENTS, MAX_ADAPTERS, MIN_RANK, MAX_RANK = 256, 32, 16, 512
 WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
-EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_workspace_bytes", "lora_proj_path", "lora_status_string")
+EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_workspace_bytes", "lora_proj_path",
+           "lora_status_string")
 
 _lib = None
 
@@ -50,6 +52,9 @@ def load():
     lib.lora_proj.restype = ctypes.c_int
     lib.lora_proj_ex.argtypes = lib.lora_proj.argtypes + [vp, vp]
     lib.lora_proj_ex.restype = ctypes.c_int
+    lib.lora_proj_multi.argtypes = (lib.lora_proj.argtypes[:9] + [ctypes.POINTER(ctypes.c_float)] +
+                                    lib.lora_proj.argtypes[10:])
+    lib.lora_proj_multi.restype = ctypes.c_int
     lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -77,7 +82,9 @@ def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, 
     """Call the C entry point with raw device addresses (ints) and host segment lists.
 
     ``events``: optional (start, stop) hipEvent_t handles recorded around the
-    output kernel (calls lora_proj_ex).  Returns the status code.
+    output kernel (calls lora_proj_ex).  ``scale``: one float for every adapter,
+    or a sequence with one scale per adapter (calls lora_proj_multi, which takes
+    no events).  Returns the status code.
     """
     lib = load()
     starts = (ctypes.c_int32 * len(seg_starts))(*[int(v) for v in seg_starts])
@@ -85,9 +92,21 @@ def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, 
     n_ad = len(A)
     a_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(a) if a else None for a in A])
     b_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(b) if b else None for b in B])
-    args = (X, starts, adapt, len(seg_adapter), W, a_arr, b_arr, n_ad, int(rank), float(scale), Y,
+    per_adapter = not isinstance(scale, numbers.Real)
+    if per_adapter:
+        scales = [float(v) for v in scale]
+        if len(scales) != n_ad:
+            raise ValueError("one scale per adapter")
+        if events is not None:
+            raise ValueError("per-adapter scales take no timing events")
+        s_arg = (ctypes.c_float * max(n_ad, 1))(*scales)
+    else:
+        s_arg = float(scale)
+    args = (X, starts, adapt, len(seg_adapter), W, a_arr, b_arr, n_ad, int(rank), s_arg, Y,
             int(M), int(N), int(K), DTYPES[dtype] if isinstance(dtype, str) else int(dtype),
             workspace, int(workspace_bytes_), stream)
+    if per_adapter:
+        return int(lib.lora_proj_multi(*args))
     if events is not None:
         return int(lib.lora_proj_ex(*args, events[0], events[1]))
     return int(lib.lora_proj(*args))
@@ -97,6 +116,7 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
               events=None):
     """Y = X W^T, plus s (X A_a^T) B_a^T on rows of segments naming adapter a.
 
+    ``scale`` is one float, or a sequence of one scale per adapter.
     X (M, K), W (N, K), A[a] (r, K), B[a] (N, r): contiguous CUDA tensors of one
     dtype (bfloat16, or float32 for the test mode).  seg_starts / seg_adapter:
     host sequences of ints.  dtype: "bf16", "f32" or "bf16_f32out" (default

@@ -104,17 +104,17 @@ const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_d
   return small_m(M) ? "decode" : "prefill";
 }
 
-lora_status lora_proj_ex(const void* X,
-                         const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
-                         const void* W,
-                         const void* const* A, const void* const* B,
-                         int32_t n_adapters, int32_t rank, float scale,
-                         void* Y,
-                         int64_t M, int64_t N, int64_t K,
-                         lora_dtype dtype,
-                         void* workspace, size_t workspace_bytes,
-                         hipStream_t stream,
-                         hipEvent_t main_start, hipEvent_t main_stop) {
+}  // extern "C"
+
+namespace {
+
+// One call.  scales[a] is adapter a's scale; when scales is NULL every adapter
+// uses `scale`.
+lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                     const void* W, const void* const* A, const void* const* B, int32_t n_adapters, int32_t rank,
+                     const float* scales, float scale, void* Y, int64_t M, int64_t N, int64_t K,
+                     lora_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
+                     hipEvent_t main_start, hipEvent_t main_stop) {
   lora_status st = check_shape(M, N, K, dtype);
   if (st != LORA_OK) return st;
   if (M == 0) return LORA_OK;
@@ -168,6 +168,7 @@ lora_status lora_proj_ex(const void* X,
       if (!aligned16(A[a]) || !aligned16(B[a])) return LORA_EINVAL;
       at.A[a] = A[a];
       at.B[a] = B[a];
+      at.scale[a] = scales ? scales[a] : scale;
     }
   }
 
@@ -215,7 +216,6 @@ lora_status lora_proj_ex(const void* X,
   p.N = int32_t(N);
   p.K = int32_t(K);
   p.rank = has_adapter ? rank : 0;
-  p.scale = scale;
   p.x_bytes = uint32_t(x_bytes);
   p.w_bytes = uint32_t(w_bytes);
   p.y_bytes = uint32_t(y_bytes);
@@ -249,7 +249,6 @@ lora_status lora_proj_ex(const void* X,
     d.N = int32_t(N);
     d.K = int32_t(K);
     d.rank = int32_t(plan_rank(rank));
-    d.scale = scale;
     d.nst = pl.nst;
     d.nrs = pl.nrs;
     d.n_used = pl.n_used;
@@ -275,6 +274,25 @@ lora_status lora_proj_ex(const void* X,
   return e == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
+}  // namespace
+
+extern "C" {
+
+lora_status lora_proj_ex(const void* X,
+                         const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                         const void* W,
+                         const void* const* A, const void* const* B,
+                         int32_t n_adapters, int32_t rank, float scale,
+                         void* Y,
+                         int64_t M, int64_t N, int64_t K,
+                         lora_dtype dtype,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream,
+                         hipEvent_t main_start, hipEvent_t main_stop) {
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, Y, M, N, K, dtype,
+                  workspace, workspace_bytes, stream, main_start, main_stop);
+}
+
 lora_status lora_proj(const void* X,
                       const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
                       const void* W,
@@ -285,8 +303,23 @@ lora_status lora_proj(const void* X,
                       lora_dtype dtype,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
-  return lora_proj_ex(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scale, Y, M, N, K, dtype,
-                      workspace, workspace_bytes, stream, nullptr, nullptr);
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, Y, M, N, K, dtype,
+                  workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+lora_status lora_proj_multi(const void* X,
+                            const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                            const void* W,
+                            const void* const* A, const void* const* B,
+                            int32_t n_adapters, int32_t rank, const float* scales,
+                            void* Y,
+                            int64_t M, int64_t N, int64_t K,
+                            lora_dtype dtype,
+                            void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  if (n_adapters > 0 && !scales) return LORA_EINVAL;
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, Y, M, N, K, dtype,
+                  workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

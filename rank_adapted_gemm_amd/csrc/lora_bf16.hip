@@ -4,7 +4,8 @@
 // request-path figure: each changed matrix runs the base product plus the
 // adapter's two thin matrices, for adapter requests only):
 //
-//   shrink  T = s X_a A_a^T on the rows of adapter segments.  T is stored as
+//   shrink  T = s_a X_a A_a^T on the rows of adapter segments (s_a the scale of
+//           adapter a).  T is stored as
 //           two bf16 halves, hi = bf16(T) and lo = bf16(T - hi), so the expand
 //           can run on bf16 MFMA while keeping T to about 2^-17 relative.
 //   main    per output tile: acc = X W^T over K, then, if the tile holds adapter
@@ -297,7 +298,8 @@ __device__ __forceinline__ void tile_of_block(int b, int ntn, int ntm, int& tn, 
 // ------------------------------------------------------------------ shrink
 // Grid: one block per (rank tile, row tile).  For every adapter segment that
 // overlaps the block's rows: acc = A_a[rank tile] X[rows]^T, then
-// T = s acc stored as bf16 hi and lo parts on the segment's rows only.
+// T = s_a acc (s_a the scale of the segment's adapter) stored as bf16 hi and lo
+// parts on the segment's rows only.
 template <class C>
 __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, AdapterTable at, int ntn, int ntm) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
@@ -340,7 +342,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
           const int jr = j0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
           float h[4], l[4];
 #pragma unroll
-          for (int e = 0; e < 4; ++e) split_hi_lo(p.scale * acc[i][j][q * 4 + e], h[e], l[e]);
+          for (int e = 0; e < 4; ++e) split_hi_lo(at.scale[a] * acc[i][j][q * 4 + e], h[e], l[e]);
           const uint32_t off = (row_ok && jr < p.rank) ? (uint32_t(m) * uint32_t(p.rank) + uint32_t(jr)) * 2u
                                                        : kMaskedOffset;
           const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};

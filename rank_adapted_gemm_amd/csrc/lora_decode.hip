@@ -11,7 +11,7 @@
 //     16*MT activation rows each).
 //   * A blocks (first in the grid, a few) each take one K range of every A_a
 //     tile and store one fp32 partial per tile.  When all of them are done
-//     they reduce T = s * X A^T between them, each a share of the
+//     they reduce T = s_a * X A_a^T between them, each a share of the
 //     (tile, 16-row) pieces, and store it as bf16 hi = bf16(T), lo =
 //     bf16(T - hi), zero on rows that name another adapter or none.
 //   * W blocks (one per remaining CU) split the W units evenly and in order
@@ -465,7 +465,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float hi, lo;
-        split_hi_lo(mine ? d.scale * sum[e] : 0.0f, hi, lo);
+        split_hi_lo(mine ? at.scale[d.slot_adapter[sl]] * sum[e] : 0.0f, hi, lo);
         hb[e] = bf16_bits(hi);
         lb[e] = bf16_bits(lo);
       }

@@ -1,7 +1,7 @@
 // fp32 test-mode kernels of the mixed-adapter LoRA projection.
 //
 // Same two launches and the same segment scheduling as the bf16 path, in fp32
-// throughout: shrink T = s X_a A_a^T (fp32 workspace), then
+// throughout: shrink T = s_a X_a A_a^T (fp32 workspace), then
 // Y = X W^T (+ T B_a^T on adapter rows).  64x64 output tiles, 256 threads with
 // a 4x4 register block each, 16-wide K slabs staged transposed in LDS, fused
 // multiply-adds in ascending k order.  Meant for tight parity checks of the
@@ -96,7 +96,7 @@ __global__ __launch_bounds__(256) void f32_shrink_kernel(ProjArgs p, SegTable st
       for (int j = 0; j < 4; ++j) {
         const int jr = j0 + tx * 4 + j;
         const bool ok = m >= lo && m < hi && jr < p.rank;
-        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, p.scale * acc[i][j]), tres,
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, at.scale[a] * acc[i][j]), tres,
                                               ok ? (uint32_t(m) * uint32_t(p.rank) + uint32_t(jr)) * 4u
                                                  : kMaskedOffset, 0, 0);
       }

@@ -22,6 +22,7 @@ struct SegTable {
 struct AdapterTable {
   const void* A[LORA_MAX_ADAPTERS];           // r x K each (device)
   const void* B[LORA_MAX_ADAPTERS];           // N x r each (device)
+  float scale[LORA_MAX_ADAPTERS];             // s of each adapter's rows
 };
 
 // Shapes and buffers of one call.  Byte extents bound every buffer access:
@@ -30,9 +31,8 @@ struct ProjArgs {
   const void* X;
   const void* W;
   void* Y;
-  void* T;            // workspace: s X A^T for adapter rows, indexed by global row
+  void* T;            // workspace: s_a X A_a^T for adapter rows, indexed by global row
   int32_t M, N, K, rank;
-  float scale;
   uint32_t x_bytes, w_bytes, y_bytes, t_bytes;
   uint32_t a_bytes, b_bytes;   // extent of every A_a / B_a
 };
@@ -66,7 +66,6 @@ struct DecodeArgs {
   uint16_t* TL;              // [n_used][M][rank] bf16 lo part of T
   uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes;
   int32_t M, N, K, rank;
-  float scale;
   int32_t nst;               // units per tile along K: ceil(K / 64)
   int32_t nrs;               // expand units per tile per half: ceil(rank / 64)
   int32_t n_used;            // adapters named by at least one row

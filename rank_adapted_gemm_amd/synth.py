@@ -112,7 +112,7 @@ class Problem:
     B: list
     seg_starts: np.ndarray
     seg_adapter: np.ndarray
-    scale: float
+    scale: object                    # one float, or a sequence with one per adapter
     dtype: str                       # "bf16" or "f32"
     X_bits: np.ndarray | None = None
     W_bits: np.ndarray | None = None
@@ -179,7 +179,7 @@ def workload_problem(name: str, layer: int = 0, proj: int = 0, x=None) -> Proble
 
 
 def random_problem(seed: int, M: int, N: int, K: int, rank: int, seg_starts, seg_adapter,
-                   n_adapters: int = 1, scale: float = 1.0, dtype: str = "bf16",
+                   n_adapters: int = 1, scale=1.0, dtype: str = "bf16",
                    sigma_x: float = 1.0, sigma_w: float = SIGMA_WAB, integer: bool = False) -> Problem:
     """A seeded problem of any shape, for parity sweeps and edge cases.
 

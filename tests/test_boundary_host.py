@@ -146,3 +146,22 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
     monkeypatch.setattr(bd, "LIB_PATH", str(tmp_path / "absent.so"))
     with pytest.raises(RuntimeError, match="missing"):
         bd.load()
+
+
+def test_per_adapter_scales_rejected_before_launch():
+    # the per-adapter entry point shares the single-scale call's checks
+    assert call(scale=[0.5], seg_starts=[1, 32, 64]) == bd.LORA_ESEGMENTS
+    assert call(scale=[0.5], A=[None]) == bd.LORA_EADAPTER
+    assert call(scale=[0.5], rank=24) == bd.LORA_EUNSUPPORTED
+    assert call(scale=[0.5], M=0, seg_starts=[0], seg_adapter=[], X=None, Y=None) == bd.LORA_OK
+    with pytest.raises(ValueError):
+        call(scale=[0.5, 1.0])                                   # one scale per adapter
+    # NULL scales with adapters present is an invalid argument
+    lib = bd.load()
+    starts = (ctypes.c_int32 * 3)(0, 32, 64)
+    adapt = (ctypes.c_int32 * 2)(-1, 0)
+    a_arr = (ctypes.c_void_p * 1)(FAKE3)
+    b_arr = (ctypes.c_void_p * 1)(FAKE4)
+    st = lib.lora_proj_multi(FAKE, starts, adapt, 2, FAKE2, a_arr, b_arr, 1, 16, None, FAKE5,
+                             64, 512, 256, bd.DTYPES["bf16"], FAKE * 320, 1 << 24, None)
+    assert st == bd.LORA_EINVAL

@@ -262,6 +262,71 @@ def test_empty_batch():
     assert tuple(y.shape) == (0, 32)
 
 
+# ------------------------------------------------------------------ per-adapter scales and ranks
+PER_ADAPTER_CASES = {
+    # prefill: three adapters, one with scale 0, a mixed tile of base and adapter rows
+    "prefill": dict(M=300, N=520, K=200, rank=48, seg_starts=[0, 5, 130, 131, 200, 300],
+                    seg_adapter=[-1, 0, 2, 1, 0], n_adapters=3, scales=[1.0, 0.0, -0.5]),
+    # decode: two adapters over 64 rows, then base rows
+    "decode": dict(M=70, N=520, K=200, rank=48, seg_starts=[0, 30, 64, 70],
+                   seg_adapter=[1, 0, -1], n_adapters=2, scales=[0.5, -2.0]),
+}
+
+
+def padded_problem(c, true_rank, seed=8):
+    """Integer problem whose adapter 1 has rank true_rank, stored zero-padded to c["rank"].
+
+    Returns (device problem with padded A_1, B_1; oracle problem with the unpadded ones).
+    """
+    c = dict(c)
+    scales = c.pop("scales")
+    p = synth.random_problem(seed, scale=scales, integer=True, **c)
+    for arr in (p.A, p.A_bits):
+        arr[1][true_rank:] = 0
+    for arr in (p.B, p.B_bits):
+        arr[1][:, true_rank:] = 0
+    q = synth.random_problem(seed, scale=scales, integer=True, **c)
+    q.A = list(p.A)
+    q.B = list(p.B)
+    q.A[1] = p.A[1][:true_rank]
+    q.B[1] = p.B[1][:, :true_rank]
+    return p, q
+
+
+@pytest.mark.parametrize("name", list(PER_ADAPTER_CASES))
+def test_per_adapter_scales_and_ranks_exact(name):
+    """Each adapter its own scale (one of them 0) and adapter 1 of rank 20 passed zero-padded:
+    the fp32 store equals the exact result and the bf16 store is its correct rounding."""
+    c = PER_ADAPTER_CASES[name]
+    p, q = padded_problem(c, true_rank=20)
+    p.name = f"per-adapter {name}"
+    log(f"case per-adapter int {name} scales={p.scale} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    assert bd.path(p.M, p.N, p.K, p.rank) == name
+    exact = lora_proj_ref(q.X, q.seg_starts, q.seg_adapter, q.W, q.A, q.B, q.scale)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(run(p, dtype="bf16")), gates.bf16_rne_of_f64(exact))
+
+
+@pytest.mark.parametrize("name", list(PER_ADAPTER_CASES))
+def test_per_adapter_scales_random(name):
+    """Gaussian inputs, distinct scales per adapter, bf16 gate against the oracle."""
+    c = dict(PER_ADAPTER_CASES[name])
+    scales = [0.25, 1.0, -0.75][:c["n_adapters"]]
+    c.pop("scales")
+    c.update(N=1000, K=520, rank=32)
+    p = synth.random_problem(23, scale=scales, **c)
+    p.name = f"per-adapter random {name}"
+    log(f"case {p.name} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    check_bf16(p, run(p), oracle(p))
+    # one common scale through the per-adapter entry point equals the single-scale call
+    dev = to_device(p)
+    same = [0.5] * c["n_adapters"]
+    assert np.array_equal(y_bits(run(p, dev_inputs=dev, scale=same)), y_bits(run(p, dev_inputs=dev, scale=0.5)))
+
+
 # ------------------------------------------------------------------ negative controls
 @pytest.mark.parametrize("arm", ["adapter_off", "scale_doubled", "base_rows_given_adapter", "boundary_off_by_one"])
 def test_negative_control_fails_gate(arm):

@@ -16,6 +16,10 @@ Nothing here re-runs that definition: each pin reaches the answer another way.
   P6  linearity in s.   P7  rows are independent (permutation).
   P8  special cases that reduce to a plain product: s = 0, A = 0, B = 0 and an
       all-base table all give X W^T.
+  P9  adapters with their own rank and scale in one batch (section 4
+      request-path figure: each request runs its own adapter's two thin
+      matrices): brute force over W + s_a B_a A_a, exact integers per adapter,
+      and a zero-padded smaller rank giving the same rows as the unpadded one.
 
 The last test plants single mistakes in copies of the oracle (a dropped or
 sign-flipped term, transposed operands, an off-by-one segment, the wrong
@@ -40,7 +44,6 @@ def brute_merged(p, rows=None):
     """Pure-Python loops over W + s B_a A_a (the merged adapted weights)."""
     M, K = p.X.shape
     N = p.W.shape[0]
-    s = float(p.scale)
     seg = list(p.seg_starts)
     out = []
     for m in (range(M) if rows is None else rows):
@@ -56,11 +59,16 @@ def brute_merged(p, rows=None):
                 w = float(p.W[n, k])
                 if a >= 0:
                     r = p.A[a].shape[0]
-                    w += s * sum(float(p.B[a][n, j]) * float(p.A[a][j, k]) for j in range(r))
+                    w += scale_of(p, a) * sum(float(p.B[a][n, j]) * float(p.A[a][j, k]) for j in range(r))
                 acc += x[k] * w
             y.append(acc)
         out.append(y)
     return np.array(out, dtype=np.float64)
+
+
+def scale_of(p, a):
+    """Adapter a's scale: the problem holds one number or one per adapter."""
+    return float(p.scale) if np.ndim(p.scale) == 0 else float(p.scale[a])
 
 
 def call(fn, p, **kw):
@@ -94,15 +102,16 @@ def int_case(scale, square=False):
 
 
 def exact_int(p):
-    """int64 merged-weight product: 2Y = X (2W + 2s B_a A_a)^T, exact for integer inputs."""
-    s2 = int(round(2 * p.scale))
-    assert s2 == 2 * p.scale
+    """int64 merged-weight product: 2Y = X (2W + 2s_a B_a A_a)^T, exact for integer inputs."""
     X = p.X.astype(np.int64)
     W2 = 2 * p.W.astype(np.int64)
     out = np.empty((p.M, p.N), dtype=np.float64)
     for g in range(len(p.seg_adapter)):
         lo, hi = p.seg_starts[g], p.seg_starts[g + 1]
         a = p.seg_adapter[g]
+        if a >= 0:
+            s2 = int(round(2 * scale_of(p, a)))
+            assert s2 == 2 * scale_of(p, a)
         Wm = W2 if a < 0 else W2 + s2 * (p.B[a].astype(np.int64) @ p.A[a].astype(np.int64))
         out[lo:hi] = (X[lo:hi] @ Wm.T).astype(np.float64) / 2.0
     return out
@@ -225,9 +234,36 @@ def pin_special(fn):
     return ok and np.array_equal(call(fn, p), plain)
 
 
+def mixed_case(scales, integer=False):
+    """Three adapters of ranks 4, 2 and 3 with their own scales, plus base rows."""
+    p = synth.random_problem(17, M=40 if integer else 9, N=12, K=20, rank=4,
+                             seg_starts=[0, 2, 3, 5, 7, 9] if not integer else [0, 8, 11, 19, 30, 40],
+                             seg_adapter=[2, 0, -1, 1, 2], n_adapters=3, scale=list(scales),
+                             integer=integer)
+    p.A[1], p.B[1] = p.A[1][:2].copy(), p.B[1][:, :2].copy()
+    p.A[2], p.B[2] = p.A[2][:3].copy(), p.B[2][:, :3].copy()
+    return p
+
+
+def pin_per_adapter(fn):
+    p = mixed_case([0.75, -1.5, 0.25])
+    if not close(call(fn, p), brute_merged(p)):
+        return False
+    for scales in ([1.0, 0.5, 2.0], [0.0, -1.0, 1.5]):
+        q = mixed_case(scales, integer=True)
+        if not np.array_equal(call(fn, q), exact_int(q)):
+            return False
+    # padding adapter 1 (rank 2) with zero rows of A and zero columns of B to rank 4
+    # leaves every partial sum exact for integer inputs, so the rows agree bit for bit
+    y = call(fn, q)
+    q.A[1] = np.concatenate([q.A[1], np.zeros((2, q.K), np.float32)])
+    q.B[1] = np.concatenate([q.B[1], np.zeros((q.N, 2), np.float32)], axis=1)
+    return np.array_equal(call(fn, q), y)
+
+
 PINS = dict(bruteforce=pin_bruteforce, rational=pin_rational, integer=pin_integer,
             onehot=pin_onehot, base_rows=pin_base_rows, linear=pin_linear,
-            permutation=pin_permutation, special=pin_special)
+            permutation=pin_permutation, special=pin_special, per_adapter=pin_per_adapter)
 
 
 def failed_pins(fn):
@@ -257,6 +293,7 @@ def _mutant(kind):
         if kind == "segment_off_by_one":
             s[1:-1] = np.minimum(s[1:-1] + 1, M)
         W64 = np.asarray(W, dtype=np.float64)
+        scales = [float(scale)] * len(A) if np.ndim(scale) == 0 else [float(v) for v in scale]
         Y = np.empty((M, W64.shape[0]))
         for g in range(len(a)):
             x = X[s[g]:s[g + 1]].astype(np.float64)
@@ -273,7 +310,9 @@ def _mutant(kind):
             B64 = np.asarray(B[ad], dtype=np.float64)
             t = x @ (A64 if kind == "A_untransposed" else A64.T)
             d = t @ (B64 if kind == "B_untransposed" else B64.T)
-            sc = {"scale_ignored": 1.0, "scale_squared": scale * scale}.get(kind, scale)
+            sc = scales[ad]
+            sc = {"scale_ignored": 1.0, "scale_squared": sc * sc, "first_scale_for_all": scales[0],
+                  "scale_by_segment": scales[g % len(scales)]}.get(kind, sc)
             Y[s[g]:s[g + 1]] = base - sc * d if kind == "sign_flipped" else base + sc * d
         return Y
     return fn
@@ -281,7 +320,7 @@ def _mutant(kind):
 
 MUTANTS = ["adapter_dropped", "sign_flipped", "scale_ignored", "scale_squared", "A_untransposed",
            "B_untransposed", "W_untransposed", "segment_off_by_one", "adapter_on_base_rows",
-           "wrong_adapter"]
+           "wrong_adapter", "first_scale_for_all", "scale_by_segment"]
 
 
 def test_unmutated_copy_passes_every_pin():
