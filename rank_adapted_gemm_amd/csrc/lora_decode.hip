@@ -434,10 +434,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       run(std::integral_constant<Kind, KIND_A>{}, Cur{0, ka0, 0, 0, 0}, nAt * (ka1 - ka0), Cur{0, 0, 0, 0, 0}, 0);
     wait_vm<0>();
     __syncthreads();
-    if (tid == 0) {
-      arrive(cA);
-      wait_for(cA, u64(d.GA));   // every A block has stored its partials
-    }
+    if (tid == 0) arrive(cA);
+    // A block with no T piece is done: it must not wait on the count either,
+    // since the call's last tile clears it once every piece is in.
+    if (b >= nAt * MT * 2) return;
+    if (tid == 0) wait_for(cA, u64(d.GA));   // every A block has stored its partials
     __syncthreads();
     // 2. T pieces (A tile g, 16-row tile mt, 16-column group rg), dealt round
     //    robin over the A blocks; each wave sums its own fragments of every A
