@@ -77,6 +77,10 @@ typedef enum lora_dtype {
 #define LORA_MAX_ADAPTERS 32
 #define LORA_MIN_RANK 16
 #define LORA_MAX_RANK 512
+/* Sliced calls (lora_proj_sliced): at most LORA_MAX_SLICES slices, each of a
+ * width that is a multiple of LORA_SLICE_ALIGN output columns. */
+#define LORA_MAX_SLICES 4
+#define LORA_SLICE_ALIGN 256
 /* Bytes at the start of every workspace reserved for the decode path's
  * counters (see lora_proj's `workspace`). */
 #define LORA_WORKSPACE_COUNTER_BYTES 65536
@@ -171,6 +175,56 @@ lora_status lora_proj_multi(const void* X,
                             lora_dtype dtype,
                             void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
+
+/*
+ * lora_proj_sliced — several projections of the same rows in one call.
+ *
+ * Projections that read the same X (the query, key and value matrices of a
+ * layer, or its gate and up matrices) are served as one matrix whose W is the
+ * concatenation of the slices' weights along N, the way the pages' server
+ * stores such groups (section 4 request-path figure: each changed matrix runs
+ * the base product plus the adapter's two thin matrices; a merged group runs
+ * that for every member).  With S = n_slices and slice s covering output
+ * columns [c_s, c_s + slice_n[s]), each adapter a brings its slices' factors
+ * stacked:
+ *
+ *   A[a]   device, (S r) x K: rows s r .. s r + r - 1 are slice s's A_{a,s}
+ *   B[a]   device, N x r: rows c_s .. c_s + slice_n[s] - 1 are slice s's B_{a,s}
+ *
+ * and rows of a segment naming adapter a get, on the columns of slice s,
+ *
+ *     Y[m, cols_s] = X[m,:] W[cols_s,:]^T + scales[a] (X[m,:] A_{a,s}^T) B_{a,s}^T
+ *
+ * which is exactly S separate lora_proj_multi calls, one per slice, with their
+ * outputs side by side.  Base-only rows get X[m,:] W^T.
+ *
+ *   n_slices     1 .. LORA_MAX_SLICES (1 is lora_proj_multi)
+ *   slice_n      HOST, n_slices int64: each a positive multiple of LORA_SLICE_ALIGN
+ *                when n_slices > 1, summing to N (else LORA_EUNSUPPORTED / LORA_EINVAL)
+ *   scales       HOST, n_adapters floats; NULL with n_adapters > 0 is LORA_EINVAL
+ *   workspace    at least lora_proj_sliced_workspace_bytes(M, N, K, rank, n_slices,
+ *                n_adapters, dtype) bytes, with lora_proj's counter-area contract
+ *
+ * Every other argument, check and guarantee is lora_proj's.  The shared
+ * intermediate X A_a^T is S r wide, so it is computed once for all slices.
+ */
+lora_status lora_proj_sliced(const void* X,
+                             const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                             const void* W,
+                             const void* const* A, const void* const* B,
+                             int32_t n_adapters, int32_t rank, const float* scales,
+                             int32_t n_slices, const int64_t* slice_n,
+                             void* Y,
+                             int64_t M, int64_t N, int64_t K,
+                             lora_dtype dtype,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/* Workspace bytes lora_proj_sliced needs (an upper bound over segment tables naming at most
+ * n_adapters adapters, counter area included; 0 for invalid arguments).  With n_slices == 1
+ * it equals lora_proj_workspace_bytes. */
+size_t lora_proj_sliced_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
+                                        int32_t n_adapters, lora_dtype dtype);
 
 /* Workspace bytes lora_proj needs for any segment table of this shape that names at most
  * n_adapters adapters (an upper bound), counter area included.  Returns 0 for invalid

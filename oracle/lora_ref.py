@@ -90,3 +90,38 @@ def lora_proj_ref(X, seg_starts, seg_adapter, W, A, B, scale, rows=None) -> np.n
         t = x @ A64.T                  # the first thin matrix: r values per row
         Y[pos] = base + scales[adapter] * (t @ B64.T)   # the second, added to the base
     return Y
+
+
+def lora_proj_sliced_ref(X, seg_starts, seg_adapter, W, A, B, scale, slice_n, rows=None) -> np.ndarray:
+    """Several projections of the same rows, their weights concatenated along N.
+
+    "two 27B models on a single RTX 5090", section 4 request-path figure: every
+    changed matrix runs the base product plus the adapter's two thin matrices.
+    A group of changed matrices that read the same rows (query, key and value;
+    gate and up) is stored as one matrix: W is the slices' weights stacked along
+    N, each A[a] stacks the slices' first thin matrices ((S r) x K, slice s in
+    rows s r .. s r + r - 1) and each B[a] stacks their second ones along N.
+    The result is, slice by slice, the plain projection of that slice's own
+    W, A and B, with the outputs side by side; the oracle computes exactly that.
+
+    slice_n: the slices' widths (summing to N).  Returns float64 (len(rows), N).
+    """
+    W = np.asarray(W)
+    widths = [int(v) for v in slice_n]
+    if any(w < 1 for w in widths) or sum(widths) != W.shape[0]:
+        raise ValueError("slice widths must be positive and sum to N")
+    S = len(widths)
+    outs = []
+    c0 = 0
+    for s, w in enumerate(widths):
+        As, Bs = [], []
+        for a in range(len(A)):
+            Aa = np.asarray(A[a])
+            if Aa.shape[0] % S:
+                raise ValueError("A must stack one r x K factor per slice")
+            r = Aa.shape[0] // S
+            As.append(Aa[s * r:(s + 1) * r])
+            Bs.append(np.asarray(B[a])[c0:c0 + w])
+        outs.append(lora_proj_ref(X, seg_starts, seg_adapter, W[c0:c0 + w], As, Bs, scale, rows=rows))
+        c0 += w
+    return np.concatenate(outs, axis=1)

@@ -19,9 +19,10 @@ STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESEGMENTS", 3: "LORA_EA
                 4: "LORA_EUNSUPPORTED", 5: "LORA_EWORKSPACE", 6: "LORA_EHIP"}
 DTYPES = {"bf16": 0, "f32": 1, "bf16_f32out": 2}
 MAX_SEGMENTS, MAX_ADAPTERS, MIN_RANK, MAX_RANK = 256, 32, 16, 512
+MAX_SLICES, SLICE_ALIGN = 4, 256
 WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
-EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_workspace_bytes", "lora_proj_path",
-           "lora_status_string")
+EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_workspace_bytes",
+           "lora_proj_sliced_workspace_bytes", "lora_proj_path", "lora_status_string")
 
 _lib = None
 
@@ -55,6 +56,11 @@ def load():
     lib.lora_proj_multi.argtypes = (lib.lora_proj.argtypes[:9] + [ctypes.POINTER(ctypes.c_float)] +
                                     lib.lora_proj.argtypes[10:])
     lib.lora_proj_multi.restype = ctypes.c_int
+    lib.lora_proj_sliced.argtypes = (lib.lora_proj_multi.argtypes[:10] + [i32, ctypes.POINTER(i64)] +
+                                     lib.lora_proj_multi.argtypes[10:])
+    lib.lora_proj_sliced.restype = ctypes.c_int
+    lib.lora_proj_sliced_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_int]
+    lib.lora_proj_sliced_workspace_bytes.restype = sz
     lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -69,8 +75,11 @@ def status_string(status: int) -> str:
     return load().lora_status_string(status).decode()
 
 
-def workspace_bytes(M: int, N: int, K: int, rank: int, n_adapters: int = 1, dtype: str = "bf16") -> int:
-    return int(load().lora_proj_workspace_bytes(M, N, K, rank, n_adapters, DTYPES[dtype]))
+def workspace_bytes(M: int, N: int, K: int, rank: int, n_adapters: int = 1, dtype: str = "bf16",
+                    n_slices: int = 1) -> int:
+    if n_slices == 1:
+        return int(load().lora_proj_workspace_bytes(M, N, K, rank, n_adapters, DTYPES[dtype]))
+    return int(load().lora_proj_sliced_workspace_bytes(M, N, K, rank, n_slices, n_adapters, DTYPES[dtype]))
 
 
 def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:
@@ -78,13 +87,15 @@ def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:
 
 
 def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, dtype,
-                  workspace=None, workspace_bytes_=0, stream=None, events=None) -> int:
+                  workspace=None, workspace_bytes_=0, stream=None, events=None, slices=None) -> int:
     """Call the C entry point with raw device addresses (ints) and host segment lists.
 
     ``events``: optional (start, stop) hipEvent_t handles recorded around the
     output kernel (calls lora_proj_ex).  ``scale``: one float for every adapter,
     or a sequence with one scale per adapter (calls lora_proj_multi, which takes
-    no events).  Returns the status code.
+    no events).  ``slices``: output-column widths of a sliced call (calls
+    lora_proj_sliced; A[a] then holds the slices' factors stacked, S*rank rows).
+    Returns the status code.
     """
     lib = load()
     starts = (ctypes.c_int32 * len(seg_starts))(*[int(v) for v in seg_starts])
@@ -92,7 +103,9 @@ def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, 
     n_ad = len(A)
     a_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(a) if a else None for a in A])
     b_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(b) if b else None for b in B])
-    per_adapter = not isinstance(scale, numbers.Real)
+    per_adapter = not isinstance(scale, numbers.Real) or slices is not None
+    if per_adapter and isinstance(scale, numbers.Real):
+        scale = [float(scale)] * n_ad
     if per_adapter:
         scales = [float(v) for v in scale]
         if len(scales) != n_ad:
@@ -105,6 +118,9 @@ def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, 
     args = (X, starts, adapt, len(seg_adapter), W, a_arr, b_arr, n_ad, int(rank), s_arg, Y,
             int(M), int(N), int(K), DTYPES[dtype] if isinstance(dtype, str) else int(dtype),
             workspace, int(workspace_bytes_), stream)
+    if slices is not None:
+        widths = (ctypes.c_int64 * max(len(slices), 1))(*[int(v) for v in slices])
+        return int(lib.lora_proj_sliced(*args[:10], len(slices), widths, *args[10:]))
     if per_adapter:
         return int(lib.lora_proj_multi(*args))
     if events is not None:
@@ -113,10 +129,12 @@ def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, 
 
 
 def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=None, dtype=None, stream=None,
-              events=None):
+              events=None, slices=None):
     """Y = X W^T, plus s (X A_a^T) B_a^T on rows of segments naming adapter a.
 
-    ``scale`` is one float, or a sequence of one scale per adapter.
+    ``scale`` is one float, or a sequence of one scale per adapter.  ``slices``:
+    widths of the output-column slices of a sliced call (A[a] is then
+    (len(slices) * r, K), slice s's factor in rows s r .. s r + r - 1).
     X (M, K), W (N, K), A[a] (r, K), B[a] (N, r): contiguous CUDA tensors of one
     dtype (bfloat16, or float32 for the test mode).  seg_starts / seg_adapter:
     host sequences of ints.  dtype: "bf16", "f32" or "bf16_f32out" (default
@@ -133,12 +151,13 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
             raise ValueError(f"inputs must be contiguous {in_t} CUDA tensors")
     M, K = X.shape
     N = W.shape[0]
-    rank = A[0].shape[0] if len(A) else 0
+    n_slices = 1 if slices is None else len(slices)
+    rank = A[0].shape[0] // n_slices if len(A) else 0
     if out is None:
         out = torch.empty((M, N), dtype=out_t, device=X.device)
     if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
         raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
-    need = workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype)
+    need = workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype, n_slices)
     if workspace is None and need:   # zero-filled: the counter area must start at zero
         workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
@@ -147,7 +166,7 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
         stream = torch.cuda.current_stream(X.device).cuda_stream
     st = lora_proj_raw(X.data_ptr(), seg_starts, seg_adapter, W.data_ptr(),
                        [a.data_ptr() for a in A], [b.data_ptr() for b in B], rank, scale,
-                       out.data_ptr(), M, N, K, dtype, ws_ptr, ws_bytes, stream, events)
+                       out.data_ptr(), M, N, K, dtype, ws_ptr, ws_bytes, stream, events, slices)
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return out

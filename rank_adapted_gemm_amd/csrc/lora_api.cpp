@@ -65,10 +65,38 @@ int64_t plan_rank(int64_t rank) { return rank_ok(rank) ? rank : 256; }
 
 // Workspace of a call: the decode path keeps split-K partials for W and for each
 // adapter named in the batch; the prefill path keeps s X A^T (4 bytes per
-// element, bf16 hi + lo or fp32) for adapter rows, indexed by global row.
-size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used, lora_dtype dtype) {
-  if (dtype != LORA_F32 && small_m(M)) return lora::decode_plan(M, N, K, plan_rank(rank), n_used).total;
-  return n_used ? LORA_WORKSPACE_COUNTER_BYTES + t_bytes(M, rank) : 0;
+// element, bf16 hi + lo or fp32) for adapter rows, indexed by global row.  T is
+// `slices` x rank wide.
+size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t slices, int64_t n_used, lora_dtype dtype) {
+  if (dtype != LORA_F32 && small_m(M))
+    return lora::decode_plan(M, N, K, plan_rank(rank), slices * plan_rank(rank), n_used).total;
+  return n_used ? LORA_WORKSPACE_COUNTER_BYTES + t_bytes(M, slices * rank) : 0;
+}
+
+// Slice table of a call: one slice of width N for a plain call; otherwise
+// 2 .. LORA_MAX_SLICES positive widths, each a multiple of LORA_SLICE_ALIGN,
+// summing to N.
+lora_status make_slices(int32_t n_slices, const int64_t* slice_n, int64_t N, lora::Slices& sl) {
+  memset(&sl, 0, sizeof(sl));
+  if (n_slices < 1 || n_slices > LORA_MAX_SLICES) return LORA_EUNSUPPORTED;
+  if (n_slices == 1) {
+    if (slice_n && slice_n[0] != N) return LORA_EINVAL;
+    sl.n = 1;
+    sl.end[0] = int32_t(N);
+    return LORA_OK;
+  }
+  if (!slice_n) return LORA_EINVAL;
+  int64_t end = 0;
+  for (int s = 0; s < n_slices; ++s) {
+    if (slice_n[s] < 1) return LORA_EINVAL;
+    if (slice_n[s] % LORA_SLICE_ALIGN != 0) return LORA_EUNSUPPORTED;
+    end += slice_n[s];
+    if (end > N) return LORA_EINVAL;
+    sl.end[s] = int32_t(end);
+  }
+  if (end != N) return LORA_EINVAL;
+  sl.n = n_slices;
+  return LORA_OK;
 }
 
 }  // namespace
@@ -88,13 +116,20 @@ const char* lora_status_string(lora_status s) {
   return "unknown status";
 }
 
-size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
-                                 lora_dtype dtype) {
+size_t lora_proj_sliced_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
+                                        int32_t n_adapters, lora_dtype dtype) {
   if (check_shape(M, N, K, dtype) != LORA_OK) return 0;
+  if (n_slices < 1 || n_slices > LORA_MAX_SLICES) return 0;
+  if (n_slices > 1 && N % LORA_SLICE_ALIGN != 0) return 0;
   if (n_adapters < 0 || n_adapters > LORA_MAX_ADAPTERS) return 0;
   if (n_adapters > 0 && !rank_ok(rank)) return 0;
   const int64_t n_used = std::min<int64_t>(n_adapters, std::max<int64_t>(M, 1));
-  return need_bytes(M, N, K, rank, n_used, dtype);
+  return need_bytes(M, N, K, rank, n_slices, n_used, dtype);
+}
+
+size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
+                                 lora_dtype dtype) {
+  return lora_proj_sliced_workspace_bytes(M, N, K, rank, 1, n_adapters, dtype);
 }
 
 const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype) {
@@ -109,13 +144,17 @@ const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_d
 namespace {
 
 // One call.  scales[a] is adapter a's scale; when scales is NULL every adapter
-// uses `scale`.
+// uses `scale`.  n_slices / slice_n cut the output columns into slices (NULL
+// and 1 for a plain call).
 lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
                      const void* W, const void* const* A, const void* const* B, int32_t n_adapters, int32_t rank,
-                     const float* scales, float scale, void* Y, int64_t M, int64_t N, int64_t K,
-                     lora_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream,
-                     hipEvent_t main_start, hipEvent_t main_stop) {
+                     const float* scales, float scale, int32_t n_slices, const int64_t* slice_n, void* Y,
+                     int64_t M, int64_t N, int64_t K, lora_dtype dtype, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop) {
   lora_status st = check_shape(M, N, K, dtype);
+  if (st != LORA_OK) return st;
+  lora::Slices sl;
+  st = make_slices(n_slices, slice_n, N, sl);
   if (st != LORA_OK) return st;
   if (M == 0) return LORA_OK;
   if (!X || !W || !Y || !aligned16(X) || !aligned16(W) || !aligned16(Y)) return LORA_EINVAL;
@@ -157,7 +196,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
   const size_t ie = in_elem_bytes(dtype), oe = out_elem_bytes(dtype);
   AdapterTable at;
   memset(&at, 0, sizeof(at));
-  const size_t a_bytes = size_t(rank > 0 ? rank : 0) * size_t(K) * ie;
+  const size_t a_bytes = size_t(rank > 0 ? rank : 0) * size_t(sl.n) * size_t(K) * ie;
   const size_t b_bytes = size_t(N) * size_t(rank > 0 ? rank : 0) * ie;
   if (has_adapter) {
     if (!rank_ok(rank)) return LORA_EUNSUPPORTED;
@@ -183,7 +222,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
       slot_adapter[n_used++] = int8_t(a);
     }
   const bool decode = dtype != LORA_F32 && small_m(M);
-  const size_t need = need_bytes(M, N, K, rank, n_used, dtype);
+  const size_t need = need_bytes(M, N, K, rank, sl.n, n_used, dtype);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return LORA_EWORKSPACE;
     if (!aligned16(workspace)) return LORA_EINVAL;
@@ -216,16 +255,18 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
   p.N = int32_t(N);
   p.K = int32_t(K);
   p.rank = has_adapter ? rank : 0;
+  p.trank = p.rank * sl.n;
+  p.sl = sl;
   p.x_bytes = uint32_t(x_bytes);
   p.w_bytes = uint32_t(w_bytes);
   p.y_bytes = uint32_t(y_bytes);
-  p.t_bytes = has_adapter && !decode ? uint32_t(t_bytes(M, rank)) : 0u;
+  p.t_bytes = has_adapter && !decode ? uint32_t(t_bytes(M, int64_t(rank) * sl.n)) : 0u;
   p.a_bytes = uint32_t(a_bytes);
   p.b_bytes = uint32_t(b_bytes);
 
   hipError_t e = hipSuccess;
   if (decode) {
-    const lora::DecodePlan pl = lora::decode_plan(M, N, K, plan_rank(rank), n_used);
+    const lora::DecodePlan pl = lora::decode_plan(M, N, K, plan_rank(rank), sl.n * plan_rank(rank), n_used);
     lora::DecodeArgs d;
     memset(&d, 0, sizeof(d));
     char* ws = static_cast<char*>(workspace);
@@ -249,6 +290,8 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     d.N = int32_t(N);
     d.K = int32_t(K);
     d.rank = int32_t(plan_rank(rank));
+    d.trank = d.rank * sl.n;
+    d.sl = sl;
     d.nst = pl.nst;
     d.nrs = pl.nrs;
     d.n_used = pl.n_used;
@@ -289,8 +332,8 @@ lora_status lora_proj_ex(const void* X,
                          void* workspace, size_t workspace_bytes,
                          hipStream_t stream,
                          hipEvent_t main_start, hipEvent_t main_stop) {
-  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, Y, M, N, K, dtype,
-                  workspace, workspace_bytes, stream, main_start, main_stop);
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, 1, nullptr, Y, M, N,
+                  K, dtype, workspace, workspace_bytes, stream, main_start, main_stop);
 }
 
 lora_status lora_proj(const void* X,
@@ -303,8 +346,8 @@ lora_status lora_proj(const void* X,
                       lora_dtype dtype,
                       void* workspace, size_t workspace_bytes,
                       hipStream_t stream) {
-  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, Y, M, N, K, dtype,
-                  workspace, workspace_bytes, stream, nullptr, nullptr);
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, 1, nullptr, Y, M, N,
+                  K, dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 lora_status lora_proj_multi(const void* X,
@@ -318,8 +361,24 @@ lora_status lora_proj_multi(const void* X,
                             void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
   if (n_adapters > 0 && !scales) return LORA_EINVAL;
-  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, Y, M, N, K, dtype,
-                  workspace, workspace_bytes, stream, nullptr, nullptr);
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, 1, nullptr, Y, M, N, K,
+                  dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+lora_status lora_proj_sliced(const void* X,
+                             const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                             const void* W,
+                             const void* const* A, const void* const* B,
+                             int32_t n_adapters, int32_t rank, const float* scales,
+                             int32_t n_slices, const int64_t* slice_n,
+                             void* Y,
+                             int64_t M, int64_t N, int64_t K,
+                             lora_dtype dtype,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (n_adapters > 0 && !scales) return LORA_EINVAL;
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, n_slices, slice_n, Y,
+                  M, N, K, dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
 }
 
 }  // extern "C"

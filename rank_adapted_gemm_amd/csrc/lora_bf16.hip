@@ -311,14 +311,14 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
   const int wn = wave % C::WN, wm = wave / C::WN;
   const i32x4 xres = make_rsrc_words(p.X, p.x_bytes);
   const auto tres = make_rsrc(p.T, p.t_bytes);
-  const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.rank) * 2u;   // T_lo follows T_hi
+  const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.trank) * 2u;   // T_lo follows T_hi
 
   for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
     const int a = st.adapter[g];
     if (a < 0) continue;
     const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
     // rows of the tile outside [lo, hi) are computed but never stored
-    const Side as{make_rsrc_words(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.rank};
+    const Side as{make_rsrc_words(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.trank};
     const Side xs{xres, uint32_t(p.K) * 2u, m0, lo, hi};
     f32x16 acc[C::FN][C::FM];
 #pragma unroll
@@ -343,8 +343,8 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
           float h[4], l[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) split_hi_lo(at.scale[a] * acc[i][j][q * 4 + e], h[e], l[e]);
-          const uint32_t off = (row_ok && jr < p.rank) ? (uint32_t(m) * uint32_t(p.rank) + uint32_t(jr)) * 2u
-                                                       : kMaskedOffset;
+          const uint32_t off = (row_ok && jr < p.trank) ? (uint32_t(m) * uint32_t(p.trank) + uint32_t(jr)) * 2u
+                                                        : kMaskedOffset;
           const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};
           const u32x2 lv{pack2(l[0], l[1]), pack2(l[2], l[3])};
           __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), tres, off, 0, 0);
@@ -385,18 +385,20 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
   }
 
   // expand: for each adapter segment overlapping the tile, stages alternate
-  // T_hi and T_lo against the same 32-wide slab of B_a
+  // T_hi and T_lo against the same 32-wide slab of B_a.  The tile's slice reads
+  // its own r columns of T (a tile never straddles two slices).
   if (has_adapter) {
-    const i32x4 tres = make_rsrc_words(p.T, p.t_bytes);
-    const uint32_t ld = uint32_t(p.rank) * 2u;
+    const uint32_t tcol = uint32_t(slice_of(p.sl, n0) * p.rank) * 2u;
+    const i32x4 tres = make_rsrc_words(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
+    const uint32_t ld = uint32_t(p.rank) * 2u, tld = uint32_t(p.trank) * 2u;
     const int lo_row0 = m0 + p.M;          // T_lo rows sit M rows after T_hi rows
     for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
       const int a = st.adapter[g];
       if (a < 0) continue;
       const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
       const Side bs{make_rsrc_words(at.B[a], p.b_bytes), ld, n0, 0, p.N};
-      const Side th{tres, ld, m0, lo, hi};
-      const Side tl{tres, ld, lo_row0, lo + p.M, hi + p.M};
+      const Side th{tres, tld, m0, lo, hi};
+      const Side tl{tres, tld, lo_row0, lo + p.M, hi + p.M};
       const int nr = 2 * ((p.rank + BK - 1) / BK);
       auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
       if constexpr (C::NW == 8) k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm);
@@ -470,7 +472,7 @@ using ShrinkSmall = Tile<64, 64, 2, 2>;
 
 template <class C>
 hipError_t launch_shrink_t(const ProjArgs& p, const SegTable& st, const AdapterTable& at, hipStream_t s) {
-  const int ntn = (p.rank + C::TN - 1) / C::TN, ntm = (p.M + C::TM - 1) / C::TM;
+  const int ntn = (p.trank + C::TN - 1) / C::TN, ntm = (p.M + C::TM - 1) / C::TM;
   ProjArgs pa = p;
   SegTable sa = st;
   AdapterTable aa = at;

@@ -114,13 +114,14 @@ struct Unit {
 
 __device__ inline Unit unit_of(const Cur& c, Kind kind, const DecodeArgs& d, const AdapterTable& at) {
   Unit x;
-  if (kind == KIND_E) {
+  if (kind == KIND_E) {   // B_a's rows of the tile against the tile's slice of T (r columns)
     x.wres = make_rsrc_words(at.B[d.slot_adapter[c.slot]], d.b_bytes);
     x.wld = uint32_t(d.rank) * 2u;
     x.wbase = uint32_t(c.key * TR) * x.wld + uint32_t(c.st) * RB;
     x.xres = make_rsrc_words(c.hl ? d.TL : d.TH, d.t_bytes);
-    x.xld = x.wld;
-    x.xbase = uint32_t(c.slot * d.M) * x.xld + uint32_t(c.st) * RB;
+    x.xld = uint32_t(d.trank) * 2u;
+    x.xbase = uint32_t(c.slot * d.M) * x.xld + uint32_t(slice_of(d.sl, c.key * TR) * d.rank) * 2u +
+              uint32_t(c.st) * RB;
   } else {
     x.wld = uint32_t(d.K) * 2u;
     if (kind == KIND_A) {
@@ -461,7 +462,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       const int m = mt * 16 + (lane & 15);
       const bool mine = m < d.M && d.row_slot[m] == sl;
       const int j = (g % d.ntA) * TR + wave * 32 + rg * 16 + 4 * (lane >> 4);
-      const bool ok = m < d.M && j < d.rank;
+      const bool ok = m < d.M && j < d.trank;
       uint32_t hb[4], lb[4];
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
@@ -470,7 +471,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
         hb[e] = bf16_bits(hi);
         lb[e] = bf16_bits(lo);
       }
-      const uint32_t off = ok ? (uint32_t(sl * d.M + m) * uint32_t(d.rank) + uint32_t(j)) * 2u : kMaskedOffset;
+      const uint32_t off = ok ? (uint32_t(sl * d.M + m) * uint32_t(d.trank) + uint32_t(j)) * 2u : kMaskedOffset;
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{hb[0] | (hb[1] << 16), hb[2] | (hb[3] << 16)}, thr, off, 0,
                                             kDeviceScope);
       __builtin_amdgcn_raw_buffer_store_b64(u32x2{lb[0] | (lb[1] << 16), lb[2] | (lb[3] << 16)}, tlr, off, 0,
@@ -510,19 +511,19 @@ const void* pick(bool f32_out) {
 
 int decode_mtiles(int64_t M) { return M <= 32 ? 2 : M <= 64 ? 4 : M <= 80 ? 5 : 8; }
 
-DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used) {
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t trank, int64_t n_used) {
   DecodePlan p;
   p.MT = decode_mtiles(M);
   p.nst = int((K + UK - 1) / UK);
   p.nrs = int((rank + UK - 1) / UK);
-  p.ntA = int((rank + TR - 1) / TR);
+  p.ntA = int((trank + TR - 1) / TR);
   p.ntW = int((N + TR - 1) / TR);
   p.n_used = int(n_used);
   const int64_t UW = int64_t(p.ntW) * p.nst;
   // A blocks: enough that one adapter's A units take each of them about 0.35
   // of a W block's units, so T is ready well before the W blocks reach the
   // expand (the A blocks also meet and reduce T after their units).  Planned
-  // for one adapter of this rank whatever the batch holds, so the W split
+  // for one adapter of this width whatever the batch holds, so the W split
   // never depends on the adapter rows.
   const double lw = double(UW) / double(kDecodeBlocks - 16);
   int ga1 = int(std::ceil(double(p.ntA) * p.nst / (0.35 * lw)));
@@ -544,7 +545,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_
   p.off_pw = p.off_pa + r256(p.pa_bytes);
   p.pw_bytes = size_t(p.ntW) * size_t(p.smaxW) * frag;
   p.off_th = p.off_pw + r256(p.pw_bytes);
-  p.t_bytes = size_t(n_used) * size_t(M) * size_t(rank) * 2;
+  p.t_bytes = size_t(n_used) * size_t(M) * size_t(trank) * 2;
   p.off_tl = p.off_th + r256(p.t_bytes);
   p.total = p.off_tl + r256(p.t_bytes);
   return p;

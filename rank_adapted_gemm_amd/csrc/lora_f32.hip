@@ -86,7 +86,7 @@ __global__ __launch_bounds__(256) void f32_shrink_kernel(ProjArgs p, SegTable st
     if (a < 0) continue;
     const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
     float acc[4][4] = {};
-    const FSide as{make_rsrc(at.A[a], p.a_bytes), uint32_t(p.K) * 4u, j0, 0, p.rank};
+    const FSide as{make_rsrc(at.A[a], p.a_bytes), uint32_t(p.K) * 4u, j0, 0, p.trank};
     const FSide xs{xres, uint32_t(p.K) * 4u, m0, lo, hi};
     accumulate(acc, as, xs, p.K, xl, wl, tid);
 #pragma unroll
@@ -95,9 +95,9 @@ __global__ __launch_bounds__(256) void f32_shrink_kernel(ProjArgs p, SegTable st
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int jr = j0 + tx * 4 + j;
-        const bool ok = m >= lo && m < hi && jr < p.rank;
+        const bool ok = m >= lo && m < hi && jr < p.trank;
         __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, at.scale[a] * acc[i][j]), tres,
-                                              ok ? (uint32_t(m) * uint32_t(p.rank) + uint32_t(jr)) * 4u
+                                              ok ? (uint32_t(m) * uint32_t(p.trank) + uint32_t(jr)) * 4u
                                                  : kMaskedOffset, 0, 0);
       }
     }
@@ -116,14 +116,15 @@ __global__ __launch_bounds__(256) void f32_main_kernel(ProjArgs p, SegTable st, 
     const FSide xs{make_rsrc(p.X, p.x_bytes), uint32_t(p.K) * 4u, m0, 0, p.M};
     accumulate(acc, ws, xs, p.K, xl, wl, tid);
   }
-  if (has_adapter) {
-    const auto tres = make_rsrc(p.T, p.t_bytes);
+  if (has_adapter) {   // the tile's slice reads its own r columns of T
+    const uint32_t tcol = uint32_t(slice_of(p.sl, n0) * p.rank) * 4u;
+    const auto tres = make_rsrc(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
     for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
       const int a = st.adapter[g];
       if (a < 0) continue;
       const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
       const FSide bs{make_rsrc(at.B[a], p.b_bytes), uint32_t(p.rank) * 4u, n0, 0, p.N};
-      const FSide ts{tres, uint32_t(p.rank) * 4u, m0, lo, hi};
+      const FSide ts{tres, uint32_t(p.trank) * 4u, m0, lo, hi};
       accumulate(acc, bs, ts, p.rank, xl, wl, tid);
     }
   }
@@ -149,7 +150,7 @@ hipError_t launch_f32_shrink(const ProjArgs& p, const SegTable& st, const Adapte
   SegTable sa = st;
   AdapterTable aa = at;
   void* args[] = {&pa, &sa, &aa};
-  const dim3 grid((p.rank + T64 - 1) / T64, (p.M + T64 - 1) / T64);
+  const dim3 grid((p.trank + T64 - 1) / T64, (p.M + T64 - 1) / T64);
   return hipLaunchKernel(reinterpret_cast<const void*>(&f32_shrink_kernel), grid, dim3(256), args, 0, stream);
 }
 

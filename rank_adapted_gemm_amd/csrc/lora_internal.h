@@ -20,19 +20,36 @@ struct SegTable {
 };
 
 struct AdapterTable {
-  const void* A[LORA_MAX_ADAPTERS];           // r x K each (device)
+  const void* A[LORA_MAX_ADAPTERS];           // (S r) x K each (device), S = number of slices
   const void* B[LORA_MAX_ADAPTERS];           // N x r each (device)
   float scale[LORA_MAX_ADAPTERS];             // s of each adapter's rows
 };
 
 // Shapes and buffers of one call.  Byte extents bound every buffer access:
 // loads past them read zero and stores past them are dropped by the hardware.
+// Output columns are cut into slices (one slice for a plain call).  Slice s
+// covers columns [slice_end[s-1], slice_end[s]) and its expand reads columns
+// [s r, s r + r) of T, whose rows are trank = S r wide.
+struct Slices {
+  int32_t n;                                  // 1 .. LORA_MAX_SLICES
+  int32_t end[LORA_MAX_SLICES];               // cumulative column ends, end[n-1] == N
+};
+
+// Slice holding output column `col`.
+__host__ __device__ inline int slice_of(const Slices& sl, int col) {
+  int s = 0;
+  while (s + 1 < sl.n && col >= sl.end[s]) ++s;
+  return s;
+}
+
 struct ProjArgs {
   const void* X;
   const void* W;
   void* Y;
   void* T;            // workspace: s_a X A_a^T for adapter rows, indexed by global row
   int32_t M, N, K, rank;
+  int32_t trank;      // width of T and rows of every A_a: slices x rank
+  Slices sl;
   uint32_t x_bytes, w_bytes, y_bytes, t_bytes;
   uint32_t a_bytes, b_bytes;   // extent of every A_a / B_a
 };
@@ -62,14 +79,16 @@ struct DecodeArgs {
   unsigned long long* cnt;   // counter area: arrivals per W tile, A blocks done, T pieces done, W tiles finished
   float* PA;                 // [A tile][A block] partials, fragment-major
   float* PW;                 // [W tile][slot]
-  uint16_t* TH;              // [n_used][M][rank] bf16 hi part of T
-  uint16_t* TL;              // [n_used][M][rank] bf16 lo part of T
+  uint16_t* TH;              // [n_used][M][trank] bf16 hi part of T
+  uint16_t* TL;              // [n_used][M][trank] bf16 lo part of T
   uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes;
   int32_t M, N, K, rank;
+  int32_t trank;             // width of T and rows of every A_a: slices x rank
+  Slices sl;
   int32_t nst;               // units per tile along K: ceil(K / 64)
   int32_t nrs;               // expand units per tile per half: ceil(rank / 64)
   int32_t n_used;            // adapters named by at least one row
-  int32_t ntA;               // A tiles per used adapter: ceil(rank / 128)
+  int32_t ntA;               // A tiles per used adapter: ceil(trank / 128)
   int32_t ntW;               // W tiles: ceil(N / 128)
   int32_t GA, GW;            // A blocks, W blocks
   int32_t smaxW;             // partial slots per W tile
@@ -85,7 +104,7 @@ struct DecodePlan {
   int GA, GW, smaxW;
   size_t off_cnt, off_pa, pa_bytes, off_pw, pw_bytes, off_th, t_bytes, off_tl, total;
 };
-DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t n_used);
+DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t trank, int64_t n_used);
 
 // Launchers (return the HIP status of the launch).
 hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at,

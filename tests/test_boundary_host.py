@@ -165,3 +165,28 @@ def test_per_adapter_scales_rejected_before_launch():
     st = lib.lora_proj_multi(FAKE, starts, adapt, 2, FAKE2, a_arr, b_arr, 1, 16, None, FAKE5,
                              64, 512, 256, bd.DTYPES["bf16"], FAKE * 320, 1 << 24, None)
     assert st == bd.LORA_EINVAL
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(slices=[256, 512]), bd.LORA_EINVAL),                  # widths do not sum to N = 512
+    (dict(slices=[0, 512]), bd.LORA_EINVAL),                    # empty slice
+    (dict(slices=[128, 384]), bd.LORA_EUNSUPPORTED),            # not a multiple of 256
+    (dict(slices=[256] * 5, N=1280), bd.LORA_EUNSUPPORTED),     # more than 4 slices
+    (dict(slices=[511]), bd.LORA_EINVAL),                       # one slice must be N wide
+    # the stacked A is 2 r rows: the plain call's workspace is too small for the sliced T
+    (dict(slices=[256, 256], M=300, seg_starts=[0, 32, 300],
+          workspace_bytes_=bd.WORKSPACE_COUNTER_BYTES + 300 * 16 * 4), bd.LORA_EWORKSPACE),
+])
+def test_sliced_rejected_before_launch(kw, code):
+    assert call(**kw) == code
+
+
+def test_sliced_workspace_query():
+    C = bd.WORKSPACE_COUNTER_BYTES
+    assert bd.workspace_bytes(16384, 15360, 5120, 256, 1, "bf16", 3) == C + 16384 * 768 * 4
+    assert bd.workspace_bytes(300, 512, 256, 16, 1, "bf16", 1) == bd.workspace_bytes(300, 512, 256, 16, 1)
+    dec1 = bd.workspace_bytes(70, 15360, 5120, 256, 1)
+    dec3 = bd.workspace_bytes(70, 15360, 5120, 256, 1, "bf16", 3)
+    assert dec3 > dec1 and dec3 % 256 == 0
+    assert bd.workspace_bytes(70, 15360, 5120, 256, 1, "bf16", 5) == 0       # too many slices
+    assert bd.workspace_bytes(70, 15000, 5120, 256, 1, "bf16", 3) == 0       # N not slice-aligned

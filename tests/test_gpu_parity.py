@@ -15,7 +15,7 @@ import pytest
 
 import gates
 from gpu_util import log, run, to_device, y_bits, y_to_numpy
-from oracle import lora_proj_ref
+from oracle import lora_proj_ref, lora_proj_sliced_ref
 from rank_adapted_gemm_amd import binding as bd
 from rank_adapted_gemm_amd import synth
 
@@ -325,6 +325,78 @@ def test_per_adapter_scales_random(name):
     dev = to_device(p)
     same = [0.5] * c["n_adapters"]
     assert np.array_equal(y_bits(run(p, dev_inputs=dev, scale=same)), y_bits(run(p, dev_inputs=dev, scale=0.5)))
+
+
+# ------------------------------------------------------------------ sliced calls
+def sliced_problem(seed, widths, rank, integer=False, **kw):
+    """A problem whose A[a] stacks one r x K factor per slice and whose B[a] is N x r."""
+    p = synth.random_problem(seed, N=sum(widths), rank=rank * len(widths), integer=integer, **kw)
+    p.B = [b[:, :rank].copy() for b in p.B]
+    if p.B_bits is not None:
+        p.B_bits = [b[:, :rank].copy() for b in p.B_bits]
+    return p
+
+
+def run_sliced(p, widths, dtype=None, scale=None):
+    import torch
+    X, W, A, B = to_device(p)
+    y = bd.lora_proj(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale if scale is None else scale,
+                     dtype=dtype or p.dtype, slices=widths)
+    torch.cuda.synchronize()
+    return y
+
+
+SLICED_CASES = {
+    # three slices, two adapters with their own scales and base rows; ragged K and rank 48
+    "prefill": dict(M=300, K=200, seg_starts=[0, 5, 130, 131, 300], seg_adapter=[-1, 0, -1, 1]),
+    "decode": dict(M=70, K=200, seg_starts=[0, 30, 64, 70], seg_adapter=[1, 0, -1]),
+}
+
+
+@pytest.mark.parametrize("name", list(SLICED_CASES))
+def test_sliced_integer_exact(name):
+    """Slices [256, 512, 256]: fp32 store equal to the exact result, bf16 store its correct rounding."""
+    widths = [256, 512, 256]
+    p = sliced_problem(51, widths, 48, integer=True, n_adapters=2, scale=[1.0, 0.5], **SLICED_CASES[name])
+    log(f"case sliced int {name} widths={widths} path={bd.path(p.M, p.N, p.K, 48)}")
+    assert bd.path(p.M, p.N, p.K, 48) == name
+    exact = lora_proj_sliced_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, widths)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    y32 = y_to_numpy(run_sliced(p, widths, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(run_sliced(p, widths, dtype="bf16")), gates.bf16_rne_of_f64(exact))
+
+
+@pytest.mark.parametrize("name", list(SLICED_CASES))
+def test_sliced_random(name):
+    """Gaussian inputs, slices [1024, 512, 512] at rank 64: bf16 gate against the oracle; the
+    fp32 test mode within its bar."""
+    widths = [1024, 512, 512]
+    p = sliced_problem(52, widths, 64, n_adapters=2, scale=[0.75, 1.0], **dict(SLICED_CASES[name], K=1024))
+    p.name = f"sliced random {name}"
+    log(f"case {p.name} path={bd.path(p.M, p.N, p.K, 64)}")
+    ref = lora_proj_sliced_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, widths)
+    check_bf16(p, run_sliced(p, widths), ref)
+    q = sliced_problem(53, widths, 64, n_adapters=2, scale=[0.75, 1.0], dtype="f32", **dict(SLICED_CASES[name], K=256))
+    q.name = f"sliced f32 {name}"
+    rep = gates.report(y_to_numpy(run_sliced(q, widths)),
+                       lora_proj_sliced_ref(q.X, q.seg_starts, q.seg_adapter, q.W, q.A, q.B, q.scale, widths))
+    log(f"  {q.name} err/rms={rep['g1']:.3e}")
+    assert rep["nonfinite"] == 0 and rep["g1"] <= gates.F32_TOL, rep
+
+
+def test_one_slice_equals_plain_call():
+    """A sliced call with one slice is the per-adapter-scale call, bit for bit, on both paths."""
+    for M, s, a in ((300, [0, 40, 300], [-1, 0]), (70, [0, 64, 70], [0, -1])):
+        p = synth.random_problem(54, M=M, N=768, K=512, rank=32, seg_starts=s, seg_adapter=a, scale=[0.5])
+        dev = to_device(p)
+        import torch
+        X, W, A, B = dev
+        y1 = bd.lora_proj(X, s, a, W, A, B, [0.5], slices=[768])
+        y2 = bd.lora_proj(X, s, a, W, A, B, [0.5])
+        torch.cuda.synchronize()
+        assert np.array_equal(y_bits(y1), y_bits(y2))
 
 
 # ------------------------------------------------------------------ negative controls

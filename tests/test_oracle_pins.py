@@ -33,7 +33,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import lora_proj_ref, validate_segments
+from oracle import lora_proj_ref, lora_proj_sliced_ref, validate_segments
 from rank_adapted_gemm_amd import synth
 
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -390,3 +390,140 @@ def test_tiny_oracle_matches_stored_values():
             assert abs(y[m, n] - float(val)) <= 1e-12 * abs(float(val)) + 1e-15
     assert abs(np.sqrt(np.mean(y[:32] ** 2)) - float(c["rms_base_rows"])) < 1e-12
     assert abs(np.sqrt(np.mean(y[32:] ** 2)) - float(c["rms_adapter_rows"])) < 1e-12
+
+
+# ------------------------------------------------------------------ sliced calls
+# Several projections of the same rows stored as one matrix (section 4 request-path figure: every
+# changed matrix of a group runs the base product plus its own two thin matrices).  The sliced oracle
+# is pinned by brute force over each slice's merged weights W_s + s_a B_{a,s} A_{a,s}, exact integers,
+# and its reduction to the plain oracle for one slice.
+def sliced_case(widths, rank, integer=False, scale=0.75, seed=41):
+    N = sum(widths)
+    p = synth.random_problem(seed, M=9 if not integer else 48, N=N, K=12 if not integer else 96,
+                             rank=rank * len(widths), seg_starts=[0, 2, 5, 9] if not integer else [0, 7, 30, 48],
+                             seg_adapter=[1, -1, 0], n_adapters=2, scale=scale, integer=integer)
+    # B_a is N x r: keep the first r columns of the drawn N x (S r) matrix
+    p.B = [b[:, :rank].copy() for b in p.B]
+    return p
+
+
+def brute_sliced(p, widths):
+    """Pure-Python loops over each slice's merged weights W_s + s_a B_{a,s} A_{a,s}."""
+    M, K = p.X.shape
+    S = len(widths)
+    ends = np.cumsum(widths)
+    out = np.zeros((M, p.W.shape[0]))
+    for m in range(M):
+        g = int(np.searchsorted(p.seg_starts, m, side="right") - 1)
+        a = int(p.seg_adapter[g])
+        for n in range(p.W.shape[0]):
+            s = int(np.searchsorted(ends, n, side="right"))
+            acc = 0.0
+            for k in range(K):
+                w = float(p.W[n, k])
+                if a >= 0:
+                    r = p.A[a].shape[0] // S
+                    w += scale_of(p, a) * sum(float(p.B[a][n, j]) * float(p.A[a][s * r + j, k]) for j in range(r))
+                acc += float(p.X[m, k]) * w
+            out[m, n] = acc
+    return out
+
+
+def call_sliced(fn, p, widths, **kw):
+    return fn(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, widths, **kw)
+
+
+def exact_int_sliced(p, widths):
+    """int64 merged product per slice, exact for integer inputs (2Y, halved at the end)."""
+    S = len(widths)
+    X = p.X.astype(np.int64)
+    out = np.empty((p.M, p.W.shape[0]))
+    c0 = 0
+    for s, w in enumerate(widths):
+        W2 = 2 * p.W[c0:c0 + w].astype(np.int64)
+        for g in range(len(p.seg_adapter)):
+            lo, hi, a = p.seg_starts[g], p.seg_starts[g + 1], p.seg_adapter[g]
+            Wm = W2
+            if a >= 0:
+                r = p.A[a].shape[0] // S
+                s2 = int(round(2 * scale_of(p, a)))
+                Wm = W2 + s2 * (p.B[a][c0:c0 + w].astype(np.int64) @ p.A[a][s * r:(s + 1) * r].astype(np.int64))
+            out[lo:hi, c0:c0 + w] = (X[lo:hi] @ Wm.T).astype(np.float64) / 2.0
+        c0 += w
+    return out
+
+
+def pin_sliced_bruteforce(fn):
+    for widths, rank in (([4, 8, 4], 2), ([6, 6], 3)):
+        p = sliced_case(widths, rank)
+        if not close(call_sliced(fn, p, widths), brute_sliced(p, widths)):
+            return False
+    return True
+
+
+def pin_sliced_integer(fn):
+    for scale in (1.0, 0.5):
+        widths = [32, 16, 32]
+        p = sliced_case(widths, 8, integer=True, scale=scale)
+        if not np.array_equal(call_sliced(fn, p, widths), exact_int_sliced(p, widths)):
+            return False
+    return True
+
+
+def pin_sliced_one_slice(fn):
+    """One slice is the plain projection, bit for bit."""
+    p = case_rect()
+    return np.array_equal(call_sliced(fn, p, [p.W.shape[0]]), call(lora_proj_ref, p))
+
+
+PINS_SLICED = dict(sliced_bruteforce=pin_sliced_bruteforce, sliced_integer=pin_sliced_integer,
+                   sliced_one_slice=pin_sliced_one_slice)
+
+
+@pytest.mark.parametrize("name", list(PINS_SLICED))
+def test_sliced_oracle_pin(name):
+    assert PINS_SLICED[name](lora_proj_sliced_ref), name
+
+
+def _sliced_mutant(kind):
+    def fn(X, seg_starts, seg_adapter, W, A, B, scale, slice_n, rows=None):
+        widths = [int(v) for v in slice_n]
+        S = len(widths)
+        outs, c0 = [], 0
+        for s, w in enumerate(widths):
+            As, Bs = [], []
+            for a in range(len(A)):
+                r = np.asarray(A[a]).shape[0] // S
+                sa = 0 if kind == "first_slice_A_everywhere" else (S - 1 - s if kind == "slices_reversed" else s)
+                As.append(np.asarray(A[a])[sa * r:(sa + 1) * r])
+                b0 = 0 if kind == "B_not_offset" else c0
+                Bs.append(np.asarray(B[a])[b0:b0 + w])
+            Ws = np.asarray(W)[c0:c0 + w]
+            if kind == "W_slice_shifted" and s > 0:
+                Ws = np.asarray(W)[c0 - 1:c0 - 1 + w]
+            outs.append(lora_proj_ref(X, seg_starts, seg_adapter, Ws, As, Bs, scale, rows=rows))
+            c0 += w
+        return np.concatenate(outs, axis=1)
+    return fn
+
+
+SLICED_MUTANTS = ["first_slice_A_everywhere", "slices_reversed", "B_not_offset", "W_slice_shifted"]
+
+
+def test_unmutated_sliced_copy_passes_every_pin():
+    f = _sliced_mutant("none")
+    assert all(pin(f) for pin in PINS_SLICED.values())
+
+
+@pytest.mark.parametrize("kind", SLICED_MUTANTS)
+def test_planted_sliced_mistake_fails_a_pin(kind):
+    f = _sliced_mutant(kind)
+    bad = []
+    for name, pin in PINS_SLICED.items():
+        try:
+            ok = pin(f)
+        except Exception:
+            ok = False
+        if not ok:
+            bad.append(name)
+    assert bad, f"sliced mutant {kind} passed every pin"
