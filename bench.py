@@ -11,7 +11,9 @@ workload, with all inputs already resident in HBM:
       fraction of the bf16 MFMA peak.
   suffix (decode line): 24 adapted layers x 7 projections, 64 adapter rows plus
       6 base-only decode rows (M = 70).  Reported in GB/s and as a fraction of
-      HBM bandwidth.
+      HBM bandwidth, twice: one call per projection, and grouped (q/k/v as one
+      sliced call and gate/up as another, the way a server stores those
+      groups; o and down alone), 4 calls per layer over the same weights.
 
 Algorithmic work per call: FLOP = 2 M N K + 2 M_a r (K + N); bytes = W + X + Y,
 plus A_a and B_a when the call has adapter rows (bf16).
@@ -89,11 +91,11 @@ def adapter_rows(seg_starts, seg_adapter):
     return int(sum(s[g + 1] - s[g] for g in range(len(seg_adapter)) if seg_adapter[g] >= 0))
 
 
-def call_work(M, Ma, N, K, r):
-    """(main-kernel flops, shrink flops, algorithmic bytes) of one projection call."""
+def call_work(M, Ma, N, K, r, S=1):
+    """(main-kernel flops, shrink flops, algorithmic bytes) of one call of S slices."""
     main = 2 * M * N * K + 2 * Ma * N * r
-    shrink = 2 * Ma * r * K
-    byts = 2 * (N * K + M * K + M * N + ((r * K + N * r) if Ma else 0))
+    shrink = 2 * Ma * S * r * K
+    byts = 2 * (N * K + M * K + M * N + ((S * r * K + N * r) if Ma else 0))
     return main, shrink, byts
 
 
@@ -111,6 +113,22 @@ def device_layer(cfg, layer, M, dev):
     return projs
 
 
+def group_layer(projs):
+    """The layer's q/k/v and gate/up as sliced calls (weights concatenated along N, A stacked)."""
+    import torch
+    by = {p["name"]: p for p in projs}
+
+    def group(name, members):
+        ps = [by[m] for m in members]
+        g = dict(name=name, K=ps[0]["K"], N=sum(p["N"] for p in ps), X=ps[0]["X"],
+                 W=torch.cat([p["W"] for p in ps]), A=torch.cat([p["A"] for p in ps]),
+                 B=torch.cat([p["B"] for p in ps]), slices=[p["N"] for p in ps])
+        for p in ps:
+            del p["W"], p["A"], p["B"]
+        return g
+    return [group("qkv", ("q", "k", "v")), by["o"], group("gate_up", ("gate", "up")), by["down"]]
+
+
 class StepRunner:
     """All calls of one step over preallocated outputs and one shared workspace."""
 
@@ -120,7 +138,8 @@ class StepRunner:
         M = layers[0][0]["X"].shape[0]
         self.M, self.Ma = M, adapter_rows(seg_starts, seg_adapter)
         self.seg_starts, self.seg_adapter, self.scale = list(seg_starts), list(seg_adapter), scale
-        ws = max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, 1) for p in layers[0])
+        ws = max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, 1, "bf16", len(p.get("slices", [0])))
+                 for p in layers[0])
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)   # counter area starts at zero
         self.outs = {}
         for projs in layers:
@@ -134,7 +153,7 @@ class StepRunner:
     def work(self):
         main = shrink = byts = 0
         for p in self.calls:
-            a, b, c = call_work(self.M, self.Ma, p["N"], p["K"], synth.RANK)
+            a, b, c = call_work(self.M, self.Ma, p["N"], p["K"], synth.RANK, len(p.get("slices", [0])))
             main, shrink, byts = main + a, shrink + b, byts + c
         return main, shrink, byts
 
@@ -145,7 +164,7 @@ class StepRunner:
                                   [p["A"].data_ptr()], [p["B"].data_ptr()], synth.RANK, self.scale,
                                   self.outs[(p["N"],)].data_ptr(), self.M, p["N"], p["K"], "bf16",
                                   ws.data_ptr(), ws.numel(), self.stream,
-                                  None if events is None else events[i])
+                                  None if events is None else events[i], p.get("slices"))
             if st != bd.LORA_OK:
                 raise bd.LoraError(st, bd.status_string(st))
 
@@ -244,25 +263,34 @@ def run_prefill(a, dev, hip):
     return dict(value=value, ms_per_step=ms_per_step, flops=step_flops, bytes=byts, roofline=roofline)
 
 
-def run_decode(a, dev, hip):
+def run_decode(a, dev, hip, grouped=False):
     import torch
     w5 = synth.WORKLOADS["suffix"]
-    log("suffix: drawing 24 layers on the device")
-    layers = [device_layer(w5["cfg"], l, w5["M"], dev) for l in range(w5["layers"])]
+    tag = "suffix grouped" if grouped else "suffix"
+    log(f"{tag}: drawing 24 layers on the device")
+    layers = []
+    for l in range(w5["layers"]):
+        projs = device_layer(w5["cfg"], l, w5["M"], dev)
+        layers.append(group_layer(projs) if grouped else projs)
     runner = StepRunner(layers, w5["seg_starts"], w5["seg_adapter"], w5["scale"], dev)
     dmain, dshrink, dbytes = runner.work()
     wall5, _ = time_steps(runner, a.decode_steps, a.warmup, hip, events=False)
     ms5 = wall5 * 1e3 / a.decode_steps
     gbs = dbytes / (ms5 / 1e3) / 1e9
-    log(f"suffix: {ms5:.3f} ms/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
+    log(f"{tag}: {ms5:.3f} ms/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
     n_calls = len(runner.calls)
     del runner, layers
     torch.cuda.empty_cache()
-    return dict(workload="suffix: 24 layers x 7 projections, 64 adapter rows + 6 base-only decode rows, r=256",
+    if grouped:
+        workload = ("suffix, grouped: 24 layers x (q/k/v sliced, o, gate/up sliced, down), "
+                    "64 adapter rows + 6 base-only decode rows, r=256")
+    else:
+        workload = "suffix: 24 layers x 7 projections, 64 adapter rows + 6 base-only decode rows, r=256"
+    return dict(workload=workload,
                 value=round(gbs, 1), unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
                 ms_per_step=round(ms5, 4), bytes_per_step=dbytes, steps=a.decode_steps,
                 tflops=round((dmain + dshrink) / (ms5 / 1e3) / 1e12, 2),
-                call_avg_us=round(ms5 * 1e3 / n_calls, 2))
+                calls_per_step=n_calls, call_avg_us=round(ms5 * 1e3 / n_calls, 2))
 
 
 # ------------------------------------------------------------------ main
@@ -275,7 +303,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
-    ap.add_argument("--only", choices=("all", "prefill", "decode"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "decode", "decode_grouped"), default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB mebibytes (reads MIB, writes MIB) five times and exit; "
@@ -306,6 +334,8 @@ def main(argv=None):
     w = synth.WORKLOADS["prefill16k"]
     pre = run_prefill(a, dev, hip) if a.only in ("all", "prefill") else {}
     decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
+    grouped = (run_decode(a, dev, hip, grouped=True)
+               if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
     hip.close()
 
     cpu = None
@@ -323,7 +353,7 @@ def main(argv=None):
                                     "rank 256, s=1",
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
-               roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode)
+               roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -351,9 +351,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 
   // Expand units read T: the first of them is fetched only once every T piece
   // is stored.
+  bool gated = false;
   auto fetch_gate = [&]() __attribute__((always_inline)) {
+    if (gated) return;
     if (tid == 0) wait_for(cT, u64(nAt * MT * 2));
     __syncthreads();
+    gated = true;
   };
 
   // Stream units through the ring: n0 units of kind K0 from cursor c0, then
@@ -482,22 +485,38 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     if (tid == 0 && done) arrive(cT, uint32_t(done));
   } else {
     const int64_t uw0 = pstart(b, UW, d.GW), uw1 = pstart(b + 1, UW, d.GW);
-    const int nw = int(uw1 - uw0);
-    // expand units of the tile this block's W units end in, split evenly
-    // over the blocks whose W units end in that tile
-    int ne = 0;
-    Cur ce{0, 0, 0, 0, 0};
-    if (nEpt > 0 && nw > 0) {
-      const int t = int((uw1 - 1) / d.nst);
-      const int64_t e_lo = pblock(int64_t(t) * d.nst, UW, d.GW);
-      const int64_t bb = pblock(int64_t(t + 1) * d.nst - 1, UW, d.GW);
-      const int64_t e_hi = pstart(bb + 1, UW, d.GW) == int64_t(t + 1) * d.nst ? bb : bb - 1;
-      const int n_end = int(e_hi - e_lo + 1), idx = int(b - e_lo);
-      const int r0 = idx * nEpt / n_end, r1 = (idx + 1) * nEpt / n_end;
-      ne = r1 - r0;
-      ce = Cur{t, r0 % d.nrs, r0 / (2 * d.nrs), 0, (r0 / d.nrs) & 1};
+    if (uw1 > uw0) {
+      // Expand units: a tile this block covers whole and runs on past (no
+      // other block touches it) gets all of them right after its W units; the
+      // block's last tile gets this block's share, split evenly among the
+      // blocks whose W units end in that tile.  Each piece of the range runs
+      // as its own sequence: W units, then the expand units of the tile they
+      // end in.
+      const int t_last = int((uw1 - 1) / d.nst);
+      int r0 = 0, r1 = 0;
+      if (nEpt > 0) {
+        const int64_t e_lo = pblock(int64_t(t_last) * d.nst, UW, d.GW);
+        const int64_t bb = pblock(int64_t(t_last + 1) * d.nst - 1, UW, d.GW);
+        const int64_t e_hi = pstart(bb + 1, UW, d.GW) == int64_t(t_last + 1) * d.nst ? bb : bb - 1;
+        const int n_end = int(e_hi - e_lo + 1), idx = int(b - e_lo);
+        r0 = idx * nEpt / n_end;
+        r1 = (idx + 1) * nEpt / n_end;
+      }
+      int t = int((uw0 + d.nst - 1) / d.nst);   // first tile that starts inside the range
+      for (int64_t u = uw0; u < uw1;) {
+        int64_t end = uw1;
+        Cur ce{t_last, r0 % d.nrs, r0 / (2 * d.nrs), 0, (r0 / d.nrs) & 1};
+        int ne = r1 - r0;
+        if (nEpt > 0 && t < t_last) {   // a whole tile: its W units, then all its expand units
+          end = int64_t(t + 1) * d.nst;
+          ce = Cur{t, 0, 0, 0, 0};
+          ne = nEpt;
+          ++t;
+        }
+        run(std::integral_constant<Kind, KIND_W>{}, Cur{int(u / d.nst), int(u % d.nst), 0, 0, 0}, int(end - u), ce, ne);
+        u = end;
+      }
     }
-    if (nw > 0) run(std::integral_constant<Kind, KIND_W>{}, Cur{int(uw0 / d.nst), int(uw0 % d.nst), 0, 0, 0}, nw, ce, ne);
   }
 }
 
@@ -528,10 +547,10 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t tr
   const double lw = double(UW) / double(kDecodeBlocks - 16);
   int ga1 = int(std::ceil(double(p.ntA) * p.nst / (0.35 * lw)));
   ga1 = std::max(1, std::min({ga1, kDecodeMaxABlocks, p.nst}));
-  // W blocks: the rest of the CUs, but at least one per W tile, so that the W
-  // units of every tile end in some block (which takes the tile's expand units).
+  // W blocks: the rest of the CUs (never more, so every block of the grid is
+  // resident at once).  A tile that one block covers whole and runs past gets
+  // its expand units from that block.
   p.GW = int(std::min<int64_t>(kDecodeBlocks - ga1, UW));
-  p.GW = std::max(p.GW, p.ntW);
   p.GA = n_used > 0 ? ga1 : 0;
   // partial slots per W tile: the most blocks that share one tile
   p.smaxW = 0;

@@ -399,6 +399,31 @@ def test_one_slice_equals_plain_call():
         assert np.array_equal(y_bits(y1), y_bits(y2))
 
 
+# ------------------------------------------------------------------ decode grids with more W tiles than blocks
+def test_decode_tiles_inside_one_block_exact():
+    """K = 64 gives one unit per W tile, so with 320 tiles most blocks cover whole tiles and run
+    past them: those tiles' expand units run right after their W units.  Integer inputs, exact."""
+    p = synth.random_problem(61, M=70, N=40960, K=64, rank=32, seg_starts=[0, 20, 64, 70], seg_adapter=[1, 0, -1],
+                             n_adapters=2, scale=[1.0, 0.5], integer=True)
+    p.name = "decode whole-tile blocks"
+    log(f"case {p.name} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    assert bd.path(p.M, p.N, p.K, p.rank) == "decode"
+    exact = oracle(p)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
+def test_decode_wide_sliced():
+    """Two 17408-wide slices (272 W tiles, more than the grid's W blocks), Gaussian inputs."""
+    widths = [17408, 17408]
+    p = sliced_problem(62, widths, 64, M=70, K=512, seg_starts=[0, 64, 70], seg_adapter=[0, -1], scale=[1.0])
+    p.name = "decode wide sliced"
+    log(f"case {p.name} path={bd.path(p.M, p.N, p.K, 64)}")
+    ref = lora_proj_sliced_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, widths)
+    check_bf16(p, run_sliced(p, widths), ref)
+
+
 # ------------------------------------------------------------------ negative controls
 @pytest.mark.parametrize("arm", ["adapter_off", "scale_doubled", "base_rows_given_adapter", "boundary_off_by_one"])
 def test_negative_control_fails_gate(arm):
