@@ -100,12 +100,13 @@ def call_work(M, Ma, N, K, r, S=1):
 
 
 # ------------------------------------------------------------------ device workloads
-def device_layer(cfg, layer, M, dev):
+def device_layer(cfg, layer, M, dev, shapes=synth.PROJECTIONS):
     """Inputs of one adapted layer drawn on the device (same shapes and sigmas as the host recipe)."""
+    widths = sorted({K for _, K, _ in shapes})
     xs = {K: synth.device_normal_bf16((M, K), 1.0, synth.seed_of(cfg, layer, proj, synth.T_X), dev)
-          for K, proj in ((5120, synth.X_NARROW), (17408, synth.X_WIDE))}
+          for K, proj in zip(widths, (synth.X_NARROW, synth.X_WIDE))}
     projs = []
-    for pi, (name, K, N) in enumerate(synth.PROJECTIONS):
+    for pi, (name, K, N) in enumerate(shapes):
         W = synth.device_normal_bf16((N, K), synth.SIGMA_WAB, synth.seed_of(cfg, layer, pi, synth.T_W), dev)
         A = synth.device_normal_bf16((synth.RANK, K), synth.SIGMA_WAB, synth.seed_of(cfg, layer, pi, synth.T_A), dev)
         B = synth.device_normal_bf16((N, synth.RANK), synth.SIGMA_WAB, synth.seed_of(cfg, layer, pi, synth.T_B), dev)
@@ -237,21 +238,21 @@ def traffic_record():
 
 
 # ------------------------------------------------------------------ the two timed workloads
-def run_prefill(a, dev, hip):
+def run_prefill(a, dev, hip, name="prefill16k"):
     import torch
-    w = synth.WORKLOADS["prefill16k"]
-    log("prefill16k: drawing inputs on the device")
-    layer = device_layer(w["cfg"], 0, w["M"], dev)
+    w = synth.WORKLOADS[name]
+    log(f"{name}: drawing inputs on the device")
+    layer = device_layer(w["cfg"], 0, w["M"], dev, synth.projections(name))
     runner = StepRunner([layer], w["seg_starts"], w["seg_adapter"], w["scale"], dev)
     main_flops, shrink_flops, byts = runner.work()
-    log(f"prefill16k: {a.warmup} warmup + {a.steps} timed steps of {len(runner.calls)} calls")
+    log(f"{name}: {a.warmup} warmup + {a.steps} timed steps of {len(runner.calls)} calls")
     wall, main_ms = time_steps(runner, a.steps, a.warmup, hip)
     ms_per_step = wall * 1e3 / a.steps
     step_flops = main_flops + shrink_flops
     value = step_flops / (ms_per_step / 1e3) / 1e12
     main_achieved = main_flops * a.steps / (main_ms.sum() / 1e3) / 1e12
     per_proj_ms = main_ms.mean(axis=0)
-    log(f"prefill16k: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s; "
+    log(f"{name}: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s; "
         + ", ".join(f"{p['name']} {t:.3f}" for p, t in zip(runner.calls, per_proj_ms)))
     roofline = dict(bound="mfma", achieved=round(main_achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(main_achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic_record(),
@@ -303,7 +304,7 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
-    ap.add_argument("--only", choices=("all", "prefill", "decode", "decode_grouped"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped"), default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB mebibytes (reads MIB, writes MIB) five times and exit; "
@@ -333,6 +334,15 @@ def main(argv=None):
     hip = HipEvents()
     w = synth.WORKLOADS["prefill16k"]
     pre = run_prefill(a, dev, hip) if a.only in ("all", "prefill") else {}
+    pre9 = run_prefill(a, dev, hip, "prefill16k_9b") if a.only in ("all", "prefill_9b") else None
+    if pre9 is not None:
+        pre9 = dict(workload="prefill16k_9b: one layer of the 9B backbone's stand-in shapes (q,o 4096->4096; "
+                             "k,v 4096->1024; gate,up 4096->12288; down 12288->4096), 16384 rows all naming "
+                             "the adapter, rank 256",
+                    value=round(pre9["value"], 2), unit="TFLOP/s", ms_per_step=round(pre9["ms_per_step"], 4),
+                    frac=round(pre9["value"] / PEAK_BF16_TFLOPS, 4),
+                    main_kernel_tflops=pre9["roofline"]["achieved"],
+                    per_projection_ms=pre9["roofline"]["per_projection_ms"])
     decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
     grouped = (run_decode(a, dev, hip, grouped=True)
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
@@ -353,7 +363,8 @@ def main(argv=None):
                                     "rank 256, s=1",
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
-               roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped)
+               roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
+               prefill_9b=pre9)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -16,6 +16,8 @@ to 32,013 tokens; the TL;DR: six chats beside a prompt grown by four lines):
   mixed      one layer, 6 base-only decode rows around a 2,048-row adapter chunk.
   stack32k   24 adapted layers, 32,768 rows, all adapter.
   suffix     24 adapted layers, a 64-row adapter suffix plus 6 base-only decode rows.
+  prefill16k_9b, suffix_9b  the same two workloads on stand-in shapes of the 9B
+             backbone the pages also adapt (one layer each; see PROJECTIONS_9B).
 
 Each adapted layer has seven projections (K -> N): q, k, v, o 5120 -> 5120;
 gate, up 5120 -> 17408; down 17408 -> 5120.
@@ -48,6 +50,18 @@ PROJECTIONS = (
     ("up", 5120, 17408),
     ("down", 17408, 5120),
 )
+# Stand-in shapes of the 9B backbone ("Clef-Flash", hidden width 4,096; its
+# key/value cache holds 4 heads of 256, so k and v are 1,024 wide).  The pages
+# print no MLP width: 12,288 (three times the hidden width) stands in.
+PROJECTIONS_9B = (
+    ("q", 4096, 4096),
+    ("k", 4096, 1024),
+    ("v", 4096, 1024),
+    ("o", 4096, 4096),
+    ("gate", 4096, 12288),
+    ("up", 4096, 12288),
+    ("down", 12288, 4096),
+)
 RANK = 256
 N_ADAPTED_LAYERS = 24
 X_NARROW, X_WIDE = 7, 8          # proj index of the layer inputs of width 5120 / 17408
@@ -64,7 +78,16 @@ WORKLOADS = {
                      layers=N_ADAPTED_LAYERS, scale=1.0),
     "suffix": dict(cfg=5, M=70, seg_starts=(0, 64, 65, 66, 67, 68, 69, 70),
                    seg_adapter=(0, -1, -1, -1, -1, -1, -1), layers=N_ADAPTED_LAYERS, scale=1.0),
+    "prefill16k_9b": dict(cfg=6, M=16384, seg_starts=(0, 16384), seg_adapter=(0,), layers=1, scale=1.0,
+                          shapes=PROJECTIONS_9B),
+    "suffix_9b": dict(cfg=7, M=70, seg_starts=(0, 64, 65, 66, 67, 68, 69, 70),
+                      seg_adapter=(0, -1, -1, -1, -1, -1, -1), layers=1, scale=1.0, shapes=PROJECTIONS_9B),
 }
+
+
+def projections(name: str):
+    """(name, K, N) of the seven projections of a workload's layers."""
+    return WORKLOADS[name].get("shapes", PROJECTIONS)
 
 
 def seed_of(cfg: int, layer: int, proj: int, tensor: int) -> int:
@@ -148,7 +171,7 @@ def tiny() -> Problem:
 
 
 def layer_input(cfg: int, layer: int, M: int, K: int):
-    proj = X_NARROW if K == 5120 else X_WIDE
+    proj = X_NARROW if K in (5120, 4096) else X_WIDE
     return normal_bf16(seed_of(cfg, layer, proj, T_X), (M, K), 1.0)
 
 
@@ -166,7 +189,7 @@ def workload_problem(name: str, layer: int = 0, proj: int = 0, x=None) -> Proble
     """
     w = WORKLOADS[name]
     cfg, M = w["cfg"], w["M"]
-    pname, K, N = PROJECTIONS[proj]
+    pname, K, N = projections(name)[proj]
     if x is None:
         x = layer_input(cfg, layer, M, K)
     (Wb, Wf), (Ab, Af), (Bb, Bf) = projection_weights(cfg, layer, proj, K, N)

@@ -118,7 +118,7 @@ def layer_inputs():
 
 
 def workload(layer_inputs, name, proj, layer=0):
-    K = synth.PROJECTIONS[proj][1]
+    K = synth.projections(name)[proj][1]
     return synth.workload_problem(name, layer=layer, proj=proj, x=layer_inputs(name, layer, K))
 
 
@@ -161,6 +161,51 @@ def test_stack32k_layer_sampled(layer_inputs, proj):
     rows = synth.sample_rows(p.M, p.seg_starts, 192, seed=200 + proj)
     ref = oracle(p, rows=rows)
     check_bf16(p, run(p), ref, rows=rows, literal=False)
+
+
+# ------------------------------------------------------------------ the 9B backbone's stand-in shapes
+@pytest.mark.parametrize("proj", range(7))
+def test_9b_suffix_decode_full(layer_inputs, proj):
+    p = workload(layer_inputs, "suffix_9b", proj)
+    log(f"case suffix_9b proj={proj} N={p.N} K={p.K} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    check_bf16(p, run(p), oracle(p))
+
+
+@pytest.mark.parametrize("proj", range(7))
+def test_9b_prefill16k_sampled(layer_inputs, proj):
+    p = workload(layer_inputs, "prefill16k_9b", proj)
+    log(f"case prefill16k_9b proj={proj} N={p.N} K={p.K}")
+    rows = synth.sample_rows(p.M, p.seg_starts, 256, seed=300 + proj)
+    check_bf16(p, run(p), oracle(p, rows=rows), rows=rows, literal=False)
+
+
+@pytest.mark.parametrize("name", ["suffix_9b", "prefill16k_9b"])
+def test_9b_qkv_sliced(layer_inputs, name):
+    """q, k and v of a 9B layer as one sliced call (slices 4096, 1024, 1024) against the plain
+    oracle of each projection: the columns of slice s equal projection s's own result."""
+    import torch
+    ps = [workload(layer_inputs, name, j) for j in range(3)]
+    widths = [p.N for p in ps]
+    cat = lambda arrs: np.ascontiguousarray(np.concatenate(arrs, axis=0))
+    X, _, _, _ = to_device(ps[0])
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    W = dev(cat([p.W_bits for p in ps]))
+    A = dev(cat([p.A_bits[0] for p in ps]))
+    B = dev(cat([p.B_bits[0] for p in ps]))
+    p0 = ps[0]
+    log(f"case {name} qkv sliced widths={widths}")
+    y = bd.lora_proj(X, list(p0.seg_starts), list(p0.seg_adapter), W, [A], [B], p0.scale, slices=widths)
+    torch.cuda.synchronize()
+    rows = None if p0.M <= 128 else synth.sample_rows(p0.M, p0.seg_starts, 128, seed=400)
+    yv = y_to_numpy(y)
+    c0 = 0
+    for p, w in zip(ps, widths):
+        ref = oracle(p, rows=rows)
+        got = yv[:, c0:c0 + w] if rows is None else yv[rows, c0:c0 + w]
+        rep = gates.report(got, ref)
+        log(f"  slice {p.name}: G2={rep['g2']:.3e}")
+        assert rep["nonfinite"] == 0 and rep["g2"] <= gates.BF16_TOL, rep
+        c0 += w
 
 
 # ------------------------------------------------------------------ invariants
