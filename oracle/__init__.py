@@ -9,4 +9,5 @@ Every function here is pinned by tests that do not re-run its own formula
 (see tests/test_oracle_pins.py): brute-force merged-weight loops, exact
 rational and exact integer results, a one-hot closed form, and invariances.
 """
-from .lora_ref import lora_proj_ref, lora_proj_sliced_ref, validate_segments  # noqa: F401
+from .lora_ref import (dequantize_q4, lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref,  # noqa: F401
+                       validate_segments)

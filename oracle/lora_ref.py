@@ -125,3 +125,39 @@ def lora_proj_sliced_ref(X, seg_starts, seg_adapter, W, A, B, scale, slice_n, ro
         outs.append(lora_proj_ref(X, seg_starts, seg_adapter, W[c0:c0 + w], As, Bs, scale, rows=rows))
         c0 += w
     return np.concatenate(outs, axis=1)
+
+
+def dequantize_q4(packed, params, K: int) -> np.ndarray:
+    """Exact values of a 4-bit weight matrix, float64 (N x K).
+
+    "two 27B models on a single RTX 5090", section 4 memory figure: the card
+    holds a 4-bit copy of the base weights beside the bf16 adapter.  The pages
+    do not print the format; this library's (W4A16, asymmetric, groups of 128
+    along K, as AutoRound writes by default): codes of row n are packed two per byte along K, code k in
+    byte k // 2, the low nibble for even k and the high nibble for odd k.  Each
+    group g of 128 consecutive k of row n has a params word params[g, n]: bits
+    0-15 a bf16 scale s, bits 16-23 a zero point z.  The weight is s (q - z).
+    """
+    packed = np.asarray(packed, dtype=np.uint8)
+    params = np.asarray(params, dtype=np.uint32)
+    N = packed.shape[0]
+    if packed.shape[1] * 2 != K or K % 128 or params.shape != (K // 128, N):
+        raise ValueError("packed must be N x K/2 and params K/128 x N, K a multiple of 128")
+    q = np.empty((N, K), dtype=np.float64)
+    q[:, 0::2] = packed & 0xF
+    q[:, 1::2] = packed >> 4
+    scale = ((params & 0xFFFF).astype(np.uint32) << 16).view(np.float32).astype(np.float64).T   # N x G
+    zero = ((params >> 16) & 0xFF).astype(np.float64).T
+    g = np.arange(K) // 128
+    return scale[:, g] * (q - zero[:, g])
+
+
+def lora_proj_q4_ref(X, seg_starts, seg_adapter, packed, params, A, B, scale, slice_n=None, rows=None):
+    """The projection with the base weights given in 4-bit form: W is their exact
+    dequantized values (dequantize_q4), and everything else is lora_proj_ref
+    (lora_proj_sliced_ref when slice_n is given)."""
+    K = np.asarray(X).shape[1]
+    W = dequantize_q4(packed, params, K)
+    if slice_n is None:
+        return lora_proj_ref(X, seg_starts, seg_adapter, W, A, B, scale, rows=rows)
+    return lora_proj_sliced_ref(X, seg_starts, seg_adapter, W, A, B, scale, slice_n, rows=rows)

@@ -277,3 +277,39 @@ def device_normal_bf16(shape, sigma: float, seed: int, device="cuda"):
     t = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
     t.mul_(sigma)
     return t.to(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- 4-bit base weights
+Q4_GROUP = 128      # weights of one row that share a scale and a zero point, along K
+
+
+def quantize_q4(W: np.ndarray):
+    """Stand-in 4-bit copy of a weight matrix (round to nearest, min/max per group).
+
+    The pages serve a 4-bit copy of the base weights (W4A16) without printing its
+    format; this draws one in the common asymmetric form: for each row n and
+    group g of 128 consecutive k, a bf16 scale s and an integer zero point z in
+    0..15, and codes q in 0..15 with w ~ s (q - z).
+
+    Returns (packed uint8 N x K/2, params uint32 K/128 x N, codes uint8 N x K,
+    scale float32 N x K/128, zero int N x K/128).  Packing: code k sits in byte
+    k // 2, low nibble for even k, high nibble for odd k.  Params word (g, n):
+    bits 0-15 the bf16 scale, bits 16-23 the zero point.
+    """
+    W = np.asarray(W, dtype=np.float64)
+    N, K = W.shape
+    if K % Q4_GROUP:
+        raise ValueError("K must be a multiple of 128")
+    G = K // Q4_GROUP
+    Wg = W.reshape(N, G, Q4_GROUP)
+    lo = np.minimum(Wg.min(axis=2), 0.0)
+    hi = np.maximum(Wg.max(axis=2), 0.0)
+    step = (hi - lo) / 15.0
+    step[step == 0] = 1.0
+    s_bits = f32_to_bf16_bits(step.astype(np.float32))
+    s = bf16_bits_to_f32(s_bits).astype(np.float64)
+    z = np.clip(np.rint(-lo / s), 0, 15).astype(np.int64)
+    q = np.clip(np.rint(Wg / s[:, :, None] + z[:, :, None]), 0, 15).astype(np.uint8).reshape(N, K)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    params = (s_bits.astype(np.uint32) | (z.astype(np.uint32) << 16)).T.copy()
+    return packed, params, q, s.astype(np.float32), z

@@ -527,3 +527,134 @@ def test_planted_sliced_mistake_fails_a_pin(kind):
         if not ok:
             bad.append(name)
     assert bad, f"sliced mutant {kind} passed every pin"
+
+
+# ------------------------------------------------------------------ 4-bit base weights
+# "two 27B models on a single RTX 5090", section 4 memory figure: a 4-bit copy of the base weights
+# beside the bf16 adapter.  dequantize_q4 is pinned by an element-wise pure-Python decoder written
+# from the format description, an exact round trip through hand-packed codes, and a one-code closed
+# form that fixes the nibble order.
+import struct
+
+from oracle import dequantize_q4, lora_proj_q4_ref
+
+
+def decode_q4_loops(packed, params, K):
+    """Element by element: code from its nibble, scale and zero from the group's word."""
+    N = packed.shape[0]
+    out = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            byte = int(packed[n, k // 2])
+            code = (byte & 0xF) if k % 2 == 0 else (byte >> 4)
+            word = int(params[k // 128, n])
+            scale = struct.unpack("<f", struct.pack("<I", (word & 0xFFFF) << 16))[0]
+            zero = (word >> 16) & 0xFF
+            out[n, k] = scale * (code - zero)
+    return out
+
+
+def pack_by_hand(codes, scales_bf16_bits, zeros):
+    """Pack codes (N x K) and per-(row, group) params with explicit loops."""
+    N, K = codes.shape
+    packed = np.zeros((N, K // 2), dtype=np.uint8)
+    for n in range(N):
+        for j in range(K // 2):
+            packed[n, j] = int(codes[n, 2 * j]) | (int(codes[n, 2 * j + 1]) << 4)
+    params = np.zeros((K // 128, N), dtype=np.uint32)
+    for n in range(N):
+        for g in range(K // 128):
+            params[g, n] = int(scales_bf16_bits[n, g]) | (int(zeros[n, g]) << 16)
+    return packed, params
+
+
+def grid_case(seed=71, N=6, K=256):
+    """Codes, power-of-two scales and zeros drawn at random: every weight s (q - z) is exact."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    codes = g.integers(0, 16, size=(N, K))
+    exps = g.integers(-6, 0, size=(N, K // 128))
+    scales = np.ldexp(1.0, exps).astype(np.float32)
+    zeros = g.integers(0, 16, size=(N, K // 128))
+    packed, params = pack_by_hand(codes, synth.f32_to_bf16_bits(scales), zeros)
+    W = np.zeros((N, K))
+    for n in range(N):
+        for k in range(K):
+            W[n, k] = float(scales[n, k // 128]) * (int(codes[n, k]) - int(zeros[n, k // 128]))
+    return packed, params, W
+
+
+def pin_q4_loops(fn):
+    W = synth.normal_f32(72, (5, 384), 0.1)
+    packed, params, *_ = synth.quantize_q4(W)
+    return np.array_equal(fn(packed, params, 384), decode_q4_loops(packed, params, 384))
+
+
+def pin_q4_grid(fn):
+    packed, params, W = grid_case()
+    return np.array_equal(fn(packed, params, 256), W)
+
+
+def pin_q4_one_code(fn):
+    """All codes equal their zero point except code k = 1 of row 2 (the high nibble of byte 0)."""
+    N, K = 4, 256
+    codes = np.full((N, K), 5)
+    codes[2, 1] = 7
+    zeros = np.full((N, K // 128), 5)
+    scales = np.full((N, K // 128), 0.25, dtype=np.float32)
+    packed, params = pack_by_hand(codes, synth.f32_to_bf16_bits(scales), zeros)
+    W = fn(packed, params, K)
+    expect = np.zeros((N, K))
+    expect[2, 1] = 0.5
+    return np.array_equal(W, expect)
+
+
+PINS_Q4 = dict(q4_loops=pin_q4_loops, q4_grid=pin_q4_grid, q4_one_code=pin_q4_one_code)
+
+
+@pytest.mark.parametrize("name", list(PINS_Q4))
+def test_q4_dequant_pin(name):
+    assert PINS_Q4[name](dequantize_q4), name
+
+
+def test_q4_projection_is_the_plain_projection_of_the_exact_weights():
+    packed, params, W = grid_case(N=8, K=256)
+    p = synth.random_problem(73, M=5, N=8, K=256, rank=4, seg_starts=[0, 2, 5], seg_adapter=[0, -1], integer=True)
+    y = lora_proj_q4_ref(p.X, p.seg_starts, p.seg_adapter, packed, params, p.A, p.B, 0.5)
+    assert np.array_equal(y, lora_proj_ref(p.X, p.seg_starts, p.seg_adapter, W, p.A, p.B, 0.5))
+    ys = lora_proj_q4_ref(p.X, p.seg_starts, p.seg_adapter, packed, params, [a * 0 for a in p.A], p.B, 0.5)
+    assert np.array_equal(ys, p.X.astype(np.float64) @ W.T)
+
+
+def _q4_mutant(kind):
+    def fn(packed, params, K):
+        packed = np.asarray(packed, dtype=np.uint8)
+        params = np.asarray(params, dtype=np.uint32)
+        N = packed.shape[0]
+        q = np.empty((N, K))
+        lo, hi = packed & 0xF, packed >> 4
+        q[:, 0::2], q[:, 1::2] = (hi, lo) if kind == "nibbles_swapped" else (lo, hi)
+        scale = ((params & 0xFFFF).astype(np.uint32) << 16).view(np.float32).astype(np.float64).T
+        zero = ((params >> 16) & 0xFF).astype(np.float64).T
+        if kind == "zero_ignored":
+            zero = zero * 0
+        g = np.arange(K) // (64 if kind == "group_of_64" else 128)
+        g = np.minimum(g, scale.shape[1] - 1)
+        if kind == "scale_of_next_row":
+            scale = np.roll(scale, 1, axis=0)
+        return scale[:, g] * (q - zero[:, g])
+    return fn
+
+
+@pytest.mark.parametrize("kind", ["nibbles_swapped", "zero_ignored", "group_of_64", "scale_of_next_row"])
+def test_planted_q4_mistake_fails_a_pin(kind):
+    f = _q4_mutant(kind)
+    assert all(pin(_q4_mutant("none")) for pin in PINS_Q4.values())
+    bad = []
+    for name, pin in PINS_Q4.items():
+        try:
+            ok = pin(f)
+        except Exception:
+            ok = False
+        if not ok:
+            bad.append(name)
+    assert bad, f"q4 mutant {kind} passed every pin"
