@@ -226,6 +226,50 @@ lora_status lora_proj_sliced(const void* X,
 size_t lora_proj_sliced_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
                                         int32_t n_adapters, lora_dtype dtype);
 
+/*
+ * lora_proj_q4 — the sliced call with the base weights in 4-bit form.
+ *
+ * "two 27B models on a single RTX 5090", section 4 memory figure: the card
+ * serves a 4-bit copy of the base weights beside the bf16 adapter.  The pages
+ * print no format; this one is W4A16 with groups of 128 along K (AutoRound's
+ * default layout):
+ *
+ *   Wq       device, N x K/2 bytes: the 4-bit codes q (0..15) of row n, two per
+ *            byte along K; code k sits in byte k/2, low nibble for even k, high
+ *            nibble for odd k
+ *   Wp       device, (K/128) x N uint32 params words: word [g][n] holds the bf16
+ *            scale s (bits 0-15) and the zero point z (bits 16-23) of the group of
+ *            k in [128 g, 128 g + 128) of row n
+ *
+ * and the base weight is W[n][k] = s (q - z).  The result is lora_proj_sliced's
+ * with that W.  The kernels round each dequantized weight to bf16 (nearest,
+ * ties to even) before it meets the bf16 activations, an error of at most half
+ * a bf16 ulp of the weight.  Batches of at most 128 rows read the codes
+ * straight from HBM (a quarter of the bf16 bytes); larger batches first expand
+ * them into a bf16 copy in the workspace, since those calls are bound by the
+ * matrix units, not by memory.
+ *
+ * Extra limits: K a multiple of 128; dtype LORA_BF16 or LORA_BF16_F32OUT (the
+ * fp32 test mode is not offered, LORA_EUNSUPPORTED).  Wp must not be NULL
+ * (LORA_EINVAL).  workspace: at least lora_proj_q4_workspace_bytes(...) bytes.
+ */
+lora_status lora_proj_q4(const void* X,
+                         const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                         const void* Wq, const void* Wp,
+                         const void* const* A, const void* const* B,
+                         int32_t n_adapters, int32_t rank, const float* scales,
+                         int32_t n_slices, const int64_t* slice_n,
+                         void* Y,
+                         int64_t M, int64_t N, int64_t K,
+                         lora_dtype dtype,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream);
+
+/* Workspace bytes of lora_proj_q4 (0 for invalid arguments).  For more than 128 rows it
+ * includes the bf16 copy of W (N K 2 bytes). */
+size_t lora_proj_q4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
+                                    int32_t n_adapters, lora_dtype dtype);
+
 /* Workspace bytes lora_proj needs for any segment table of this shape that names at most
  * n_adapters adapters (an upper bound), counter area included.  Returns 0 for invalid
  * arguments.  Batches of at most 128 rows (the decode path) always need a workspace, for its

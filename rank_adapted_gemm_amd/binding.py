@@ -21,8 +21,9 @@ DTYPES = {"bf16": 0, "f32": 1, "bf16_f32out": 2}
 MAX_SEGMENTS, MAX_ADAPTERS, MIN_RANK, MAX_RANK = 256, 32, 16, 512
 MAX_SLICES, SLICE_ALIGN = 4, 256
 WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
-EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_workspace_bytes",
-           "lora_proj_sliced_workspace_bytes", "lora_proj_path", "lora_status_string")
+EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_q4",
+           "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
+           "lora_proj_path", "lora_status_string")
 
 _lib = None
 
@@ -61,6 +62,10 @@ def load():
     lib.lora_proj_sliced.restype = ctypes.c_int
     lib.lora_proj_sliced_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_int]
     lib.lora_proj_sliced_workspace_bytes.restype = sz
+    lib.lora_proj_q4.argtypes = lib.lora_proj_sliced.argtypes[:5] + [vp] + lib.lora_proj_sliced.argtypes[5:]
+    lib.lora_proj_q4.restype = ctypes.c_int
+    lib.lora_proj_q4_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_int]
+    lib.lora_proj_q4_workspace_bytes.restype = sz
     lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -80,6 +85,68 @@ def workspace_bytes(M: int, N: int, K: int, rank: int, n_adapters: int = 1, dtyp
     if n_slices == 1:
         return int(load().lora_proj_workspace_bytes(M, N, K, rank, n_adapters, DTYPES[dtype]))
     return int(load().lora_proj_sliced_workspace_bytes(M, N, K, rank, n_slices, n_adapters, DTYPES[dtype]))
+
+
+def q4_workspace_bytes(M: int, N: int, K: int, rank: int, n_adapters: int = 1, dtype: str = "bf16",
+                       n_slices: int = 1) -> int:
+    return int(load().lora_proj_q4_workspace_bytes(M, N, K, rank, n_slices, n_adapters, DTYPES[dtype]))
+
+
+def lora_proj_q4_raw(X, seg_starts, seg_adapter, Wq, Wp, A, B, rank, scales, Y, M, N, K, dtype,
+                     workspace=None, workspace_bytes_=0, stream=None, slices=None) -> int:
+    """lora_proj_q4 with raw device addresses (ints); ``scales`` one float per adapter."""
+    lib = load()
+    starts = (ctypes.c_int32 * len(seg_starts))(*[int(v) for v in seg_starts])
+    adapt = (ctypes.c_int32 * max(len(seg_adapter), 1))(*[int(v) for v in seg_adapter])
+    n_ad = len(A)
+    a_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(a) if a else None for a in A])
+    b_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(b) if b else None for b in B])
+    if isinstance(scales, numbers.Real):
+        scales = [float(scales)] * n_ad
+    if len(scales) != n_ad:
+        raise ValueError("one scale per adapter")
+    s_arg = (ctypes.c_float * max(n_ad, 1))(*[float(v) for v in scales])
+    widths = list(slices) if slices is not None else [int(N)]
+    w_arg = (ctypes.c_int64 * len(widths))(*[int(v) for v in widths])
+    return int(lib.lora_proj_q4(X, starts, adapt, len(seg_adapter), Wq, Wp, a_arr, b_arr, n_ad, int(rank), s_arg,
+                                len(widths), w_arg, Y, int(M), int(N), int(K),
+                                DTYPES[dtype] if isinstance(dtype, str) else int(dtype), workspace,
+                                int(workspace_bytes_), stream))
+
+
+def lora_proj_q4(X, seg_starts, seg_adapter, Wq, Wp, A, B, scale, out=None, workspace=None, dtype="bf16",
+                 stream=None, slices=None):
+    """Y with the base weights in 4-bit form: Wq (N, K/2) uint8 codes, Wp (K/128, N) int32 params words.
+
+    Other arguments as lora_proj; returns Y (M, N).
+    """
+    import torch
+    M, K = X.shape
+    N = Wq.shape[0]
+    for t in (X, *A, *B):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("X, A, B must be contiguous bfloat16 CUDA tensors")
+    for t in (Wq, Wp):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("Wq and Wp must be contiguous CUDA tensors")
+    n_slices = 1 if slices is None else len(slices)
+    rank = A[0].shape[0] // n_slices if len(A) else 0
+    out_t = torch.bfloat16 if dtype == "bf16" else torch.float32
+    if out is None:
+        out = torch.empty((M, N), dtype=out_t, device=X.device)
+    need = q4_workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype, n_slices)
+    if workspace is None and need:
+        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device).cuda_stream
+    st = lora_proj_q4_raw(X.data_ptr(), seg_starts, seg_adapter, Wq.data_ptr(), Wp.data_ptr(),
+                          [a.data_ptr() for a in A], [b.data_ptr() for b in B], rank, scale, out.data_ptr(),
+                          M, N, K, dtype, ws_ptr, ws_bytes, stream, slices)
+    if st != LORA_OK:
+        raise LoraError(st, status_string(st))
+    return out
 
 
 def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:

@@ -67,10 +67,24 @@ int64_t plan_rank(int64_t rank) { return rank_ok(rank) ? rank : 256; }
 // adapter named in the batch; the prefill path keeps s X A^T (4 bytes per
 // element, bf16 hi + lo or fp32) for adapter rows, indexed by global row.  T is
 // `slices` x rank wide.
-size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t slices, int64_t n_used, lora_dtype dtype) {
+size_t r256(size_t x) { return (x + 255) & ~size_t(255); }
+
+// With 4-bit weights the prefill path also keeps a bf16 copy of W after T.
+size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t slices, int64_t n_used, lora_dtype dtype,
+                  bool q4 = false) {
   if (dtype != LORA_F32 && small_m(M))
     return lora::decode_plan(M, N, K, plan_rank(rank), slices * plan_rank(rank), n_used).total;
+  if (q4)
+    return LORA_WORKSPACE_COUNTER_BYTES + (n_used ? r256(t_bytes(M, slices * rank)) : 0) + size_t(N) * size_t(K) * 2;
   return n_used ? LORA_WORKSPACE_COUNTER_BYTES + t_bytes(M, slices * rank) : 0;
+}
+
+// Extra checks of a call with 4-bit weights: the bf16 kernels only, K a
+// multiple of the 128-wide group.
+lora_status check_q4(int64_t K, lora_dtype dtype) {
+  if (dtype == LORA_F32) return LORA_EUNSUPPORTED;
+  if (K % 128 != 0) return LORA_EUNSUPPORTED;
+  return LORA_OK;
 }
 
 // Slice table of a call: one slice of width N for a plain call; otherwise
@@ -127,6 +141,17 @@ size_t lora_proj_sliced_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t
   return need_bytes(M, N, K, rank, n_slices, n_used, dtype);
 }
 
+size_t lora_proj_q4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
+                                    int32_t n_adapters, lora_dtype dtype) {
+  if (check_shape(M, N, K, dtype) != LORA_OK || check_q4(K, dtype) != LORA_OK) return 0;
+  if (n_slices < 1 || n_slices > LORA_MAX_SLICES) return 0;
+  if (n_slices > 1 && N % LORA_SLICE_ALIGN != 0) return 0;
+  if (n_adapters < 0 || n_adapters > LORA_MAX_ADAPTERS) return 0;
+  if (n_adapters > 0 && !rank_ok(rank)) return 0;
+  const int64_t n_used = std::min<int64_t>(n_adapters, std::max<int64_t>(M, 1));
+  return need_bytes(M, N, K, rank, n_slices, n_used, dtype, true);
+}
+
 size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
                                  lora_dtype dtype) {
   return lora_proj_sliced_workspace_bytes(M, N, K, rank, 1, n_adapters, dtype);
@@ -145,19 +170,23 @@ namespace {
 
 // One call.  scales[a] is adapter a's scale; when scales is NULL every adapter
 // uses `scale`.  n_slices / slice_n cut the output columns into slices (NULL
-// and 1 for a plain call).
+// and 1 for a plain call).  WP non-null: W holds 4-bit codes and WP their
+// params words (lora_proj_q4).
 lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
                      const void* W, const void* const* A, const void* const* B, int32_t n_adapters, int32_t rank,
                      const float* scales, float scale, int32_t n_slices, const int64_t* slice_n, void* Y,
                      int64_t M, int64_t N, int64_t K, lora_dtype dtype, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop) {
+                     hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop, const void* WP = nullptr) {
   lora_status st = check_shape(M, N, K, dtype);
   if (st != LORA_OK) return st;
+  const bool q4 = WP != nullptr;
+  if (q4 && (st = check_q4(K, dtype)) != LORA_OK) return st;
   lora::Slices sl;
   st = make_slices(n_slices, slice_n, N, sl);
   if (st != LORA_OK) return st;
   if (M == 0) return LORA_OK;
   if (!X || !W || !Y || !aligned16(X) || !aligned16(W) || !aligned16(Y)) return LORA_EINVAL;
+  if (q4 && !aligned16(WP)) return LORA_EINVAL;
   if (n_adapters < 0) return LORA_EINVAL;
   if (n_adapters > LORA_MAX_ADAPTERS) return LORA_EUNSUPPORTED;
   if (n_adapters > 0 && (!A || !B)) return LORA_EINVAL;
@@ -222,7 +251,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
       slot_adapter[n_used++] = int8_t(a);
     }
   const bool decode = dtype != LORA_F32 && small_m(M);
-  const size_t need = need_bytes(M, N, K, rank, sl.n, n_used, dtype);
+  const size_t need = need_bytes(M, N, K, rank, sl.n, n_used, dtype, q4);
   if (need > 0) {
     if (!workspace || workspace_bytes < need) return LORA_EWORKSPACE;
     if (!aligned16(workspace)) return LORA_EINVAL;
@@ -232,8 +261,11 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
   // ---- the output may not overlap anything the call reads or the workspace
   const size_t y_bytes = size_t(M) * size_t(N) * oe;
   const size_t x_bytes = size_t(M) * size_t(K) * ie;
-  const size_t w_bytes = size_t(N) * size_t(K) * ie;
+  const size_t w_bytes = q4 ? size_t(N) * size_t(K) / 2 : size_t(N) * size_t(K) * ie;
+  const size_t wp_bytes = q4 ? size_t(K / 128) * size_t(N) * 4 : 0;
   if (overlaps(Y, y_bytes, X, x_bytes) || overlaps(Y, y_bytes, W, w_bytes)) return LORA_EINVAL;
+  if (q4 && (overlaps(Y, y_bytes, WP, wp_bytes) || (need > 0 && overlaps(WP, wp_bytes, workspace, need))))
+    return LORA_EINVAL;
   if (need > 0 && (overlaps(Y, y_bytes, workspace, need) || overlaps(X, x_bytes, workspace, need) ||
                    overlaps(W, w_bytes, workspace, need)))
     return LORA_EINVAL;
@@ -272,6 +304,8 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     char* ws = static_cast<char*>(workspace);
     d.X = X;
     d.W = W;
+    d.WP = WP;
+    d.wp_bytes = uint32_t(wp_bytes);
     d.Y = Y;
     d.cnt = reinterpret_cast<unsigned long long*>(ws + pl.off_cnt);
     d.PA = reinterpret_cast<float*>(ws + pl.off_pa);
@@ -309,7 +343,14 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     if (has_adapter) e = lora::launch_f32_shrink(p, tbl, at, stream);
     if (e == hipSuccess) e = lora::launch_f32_main(p, tbl, at, has_adapter, stream, main_start, main_stop);
   } else {
-    if (has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, false, stream);
+    if (q4) {   // expand the 4-bit weights into a bf16 copy after T, then run the bf16 kernels
+      char* wcopy = static_cast<char*>(workspace) + LORA_WORKSPACE_COUNTER_BYTES +
+                    (has_adapter ? r256(t_bytes(M, int64_t(rank) * sl.n)) : 0);
+      e = lora::launch_q4_dequant(W, WP, wcopy, N, K, stream);
+      p.W = wcopy;
+      p.w_bytes = uint32_t(size_t(N) * size_t(K) * 2);
+    }
+    if (e == hipSuccess && has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, false, stream);
     if (e == hipSuccess)
       e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, false, stream, main_start,
                                  main_stop);
@@ -363,6 +404,23 @@ lora_status lora_proj_multi(const void* X,
   if (n_adapters > 0 && !scales) return LORA_EINVAL;
   return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, 1, nullptr, Y, M, N, K,
                   dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+lora_status lora_proj_q4(const void* X,
+                         const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                         const void* Wq, const void* Wp,
+                         const void* const* A, const void* const* B,
+                         int32_t n_adapters, int32_t rank, const float* scales,
+                         int32_t n_slices, const int64_t* slice_n,
+                         void* Y,
+                         int64_t M, int64_t N, int64_t K,
+                         lora_dtype dtype,
+                         void* workspace, size_t workspace_bytes,
+                         hipStream_t stream) {
+  if (!Wp) return LORA_EINVAL;
+  if (n_adapters > 0 && !scales) return LORA_EINVAL;
+  return run_call(X, seg_starts, seg_adapter, n_seg, Wq, A, B, n_adapters, rank, scales, 0.0f, n_slices, slice_n, Y,
+                  M, N, K, dtype, workspace, workspace_bytes, stream, nullptr, nullptr, Wp);
 }
 
 lora_status lora_proj_sliced(const void* X,

@@ -147,7 +147,10 @@ __device__ inline void wait_for(u64* c, u64 want) {
   }
 }
 
-template <int MT, bool F32_OUT>
+// Q4: the base weights come as 4-bit codes plus per-group params (see
+// lora_proj_q4); W units then carry 4 KiB of codes and their params instead of
+// 16 KiB of bf16, and the multiply dequantizes the weight fragments to bf16.
+template <int MT, bool F32_OUT, bool Q4>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable at) {
   using G = DG<MT>;
   __shared__ __attribute__((aligned(1024))) char smem[G::NS * G::STAGE];
@@ -204,7 +207,19 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   auto issue = [&](int slot, const Cur& c, Kind kind) __attribute__((always_inline)) {
     const Unit x = unit_of(c, kind, d, at);
     const uint32_t dst = lbase + uint32_t(slot) * G::STAGE;
-    {
+    if (Q4 && kind == KIND_W) {
+      // wave w's 4 KiB: codes of its 32 rows (32 bytes each, row-major), then
+      // their params words (4 bytes each); two more masked loads keep every
+      // wave at four weight-side loads per unit, like the bf16 units
+      const uint32_t kb = uint32_t(d.K) / 2u;                       // code bytes per row
+      const uint32_t row0 = uint32_t(c.key * TR + 32 * wave);
+      const uint32_t code_off[1] = {(row0 + uint32_t(lane >> 1)) * kb + uint32_t(c.st) * 32u + uint32_t(lane & 1) * 16u};
+      dma16_group<1>(make_rsrc_words(d.W, d.w_bytes), code_off, dst + uint32_t(4 * wave) * 1024u);
+      const uint32_t g = uint32_t(c.st) / 2u;                        // 128-wide group of the unit
+      const uint32_t prm_off[3] = {lane < 8 ? (g * uint32_t(d.N) + row0 + uint32_t(lane) * 4u) * 4u : kDmaMaskedOffset,
+                                   kDmaMaskedOffset, kDmaMaskedOffset};
+      dma16_group<3>(make_rsrc_words(d.WP, d.wp_bytes), prm_off, dst + uint32_t(4 * wave + 1) * 1024u);
+    } else {
       uint32_t off[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -393,8 +408,24 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       for (int j = 0; j < 2; ++j) {
         const int ch = 4 * j + (lane >> 4);
         bf16x8 a[2], bx[MT];
+        if constexpr (Q4 && K == KIND_W) {
+          // 8 codes of row 16 rg + lane % 16 (of this wave's 32), k = 32 j + 8 (lane / 16) ..,
+          // dequantized with the row's group params: w = s (q - z), rounded to bf16
+          const char* wq = ws + wave * 4096;
 #pragma unroll
-        for (int rg = 0; rg < 2; ++rg) a[rg] = frag(ws, wave * 32 + rg * 16 + (lane & 15), ch);
+          for (int rg = 0; rg < 2; ++rg) {
+            const int rr = rg * 16 + (lane & 15);
+            const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + rr * 32 + j * 16 + (lane >> 4) * 4);
+            const uint32_t prm = *reinterpret_cast<const uint32_t*>(wq + 1024 + rr * 4);
+            const float sc = __uint_as_float(prm << 16);
+            const float zp = float((prm >> 16) & 0xFFu);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) a[rg][e] = static_cast<__bf16>(sc * (float((codes >> (4 * e)) & 0xFu) - zp));
+          }
+        } else {
+#pragma unroll
+          for (int rg = 0; rg < 2; ++rg) a[rg] = frag(ws, wave * 32 + rg * 16 + (lane & 15), ch);
+        }
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) bx[mt] = frag(xs, mt * 16 + (lane & 15), ch);
         if (tail && e0 + ch * 8 >= lim) {
@@ -521,9 +552,12 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 }
 
 template <int MT>
-const void* pick(bool f32_out) {
-  return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true>)
-                 : reinterpret_cast<const void*>(&decode_kernel<MT, false>);
+const void* pick(bool f32_out, bool q4) {
+  if (q4)
+    return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, true>)
+                   : reinterpret_cast<const void*>(&decode_kernel<MT, false, true>);
+  return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, false>)
+                 : reinterpret_cast<const void*>(&decode_kernel<MT, false, false>);
 }
 
 }  // namespace
@@ -572,8 +606,11 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t tr
 
 hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const void* k = MT == 2 ? pick<2>(f32_out) : MT == 4 ? pick<4>(f32_out) : MT == 5 ? pick<5>(f32_out)
-                                                                                   : pick<8>(f32_out);
+  const bool q4 = d.WP != nullptr;
+  const void* k = MT == 2   ? pick<2>(f32_out, q4)
+                  : MT == 4 ? pick<4>(f32_out, q4)
+                  : MT == 5 ? pick<5>(f32_out, q4)
+                            : pick<8>(f32_out, q4);
   DecodeArgs dd = d;
   AdapterTable aa = at;
   void* args[] = {&dd, &aa};

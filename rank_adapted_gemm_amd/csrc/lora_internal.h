@@ -74,7 +74,8 @@ constexpr int kDecodeMaxABlocks = 32;   // blocks that compute T = s X A^T
 
 struct DecodeArgs {
   const void* X;
-  const void* W;
+  const void* W;             // bf16 weights, or 4-bit codes when WP is set
+  const void* WP;            // 4-bit params words [K/128][N], or null for bf16 weights
   void* Y;
   unsigned long long* cnt;   // counter area: arrivals per W tile, A blocks done, T pieces done, W tiles finished
   float* PA;                 // [A tile][A block] partials, fragment-major
@@ -82,6 +83,7 @@ struct DecodeArgs {
   uint16_t* TH;              // [n_used][M][trank] bf16 hi part of T
   uint16_t* TL;              // [n_used][M][trank] bf16 lo part of T
   uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes;
+  uint32_t wp_bytes;
   int32_t M, N, K, rank;
   int32_t trank;             // width of T and rows of every A_a: slices x rank
   Slices sl;
@@ -114,6 +116,8 @@ hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const Adapter
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop);
+// 4-bit weights: dequantize codes + params (N x K) into bf16 W (prefill path).
+hipError_t launch_q4_dequant(const void* codes, const void* params, void* w, int64_t N, int64_t K, hipStream_t stream);
 hipError_t launch_f32_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
                              hipStream_t stream);
 hipError_t launch_f32_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at,

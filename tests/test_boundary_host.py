@@ -190,3 +190,33 @@ def test_sliced_workspace_query():
     assert dec3 > dec1 and dec3 % 256 == 0
     assert bd.workspace_bytes(70, 15360, 5120, 256, 1, "bf16", 5) == 0       # too many slices
     assert bd.workspace_bytes(70, 15000, 5120, 256, 1, "bf16", 3) == 0       # N not slice-aligned
+
+
+def q4_call(**kw):
+    a = dict(X=FAKE, seg_starts=[0, 32, 64], seg_adapter=[-1, 0], Wq=FAKE2, Wp=FAKE2 + (1 << 19), A=[FAKE3],
+             B=[FAKE4], rank=16, scales=[0.5], Y=FAKE5, M=64, N=512, K=256, dtype="bf16", workspace=FAKE * 320,
+             workspace_bytes_=1 << 24, stream=None)
+    a.update(kw)
+    return bd.lora_proj_q4_raw(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(Wp=None), bd.LORA_EINVAL),
+    (dict(dtype="f32"), bd.LORA_EUNSUPPORTED),       # no fp32 test mode for 4-bit weights
+    (dict(K=192), bd.LORA_EUNSUPPORTED),             # K not a multiple of the 128-wide group
+    (dict(Wp=FAKE2 + 8), bd.LORA_EINVAL),            # misaligned params
+    (dict(Y=FAKE2 + 4096), bd.LORA_EINVAL),          # Y overlaps the codes
+    (dict(M=300, seg_starts=[0, 32, 300], workspace_bytes_=bd.WORKSPACE_COUNTER_BYTES + 300 * 16 * 4),
+     bd.LORA_EWORKSPACE),                            # the prefill path also needs the bf16 copy of W
+])
+def test_q4_rejected_before_launch(kw, code):
+    assert q4_call(**kw) == code
+
+
+def test_q4_workspace_query():
+    C = bd.WORKSPACE_COUNTER_BYTES
+    assert bd.q4_workspace_bytes(16384, 5120, 5120, 256) == C + 16384 * 256 * 4 + 5120 * 5120 * 2
+    assert bd.q4_workspace_bytes(16384, 5120, 5120, 256, 0) == C + 5120 * 5120 * 2
+    assert bd.q4_workspace_bytes(70, 5120, 5120, 256) == bd.workspace_bytes(70, 5120, 5120, 256)
+    assert bd.q4_workspace_bytes(70, 5120, 5000, 256) == 0
+    assert bd.q4_workspace_bytes(70, 5120, 5120, 256, 1, "f32") == 0

@@ -15,7 +15,7 @@ import pytest
 
 import gates
 from gpu_util import log, run, to_device, y_bits, y_to_numpy
-from oracle import lora_proj_ref, lora_proj_sliced_ref
+from oracle import lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref
 from rank_adapted_gemm_amd import binding as bd
 from rank_adapted_gemm_amd import synth
 
@@ -467,6 +467,76 @@ def test_decode_wide_sliced():
     log(f"case {p.name} path={bd.path(p.M, p.N, p.K, 64)}")
     ref = lora_proj_sliced_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, widths)
     check_bf16(p, run_sliced(p, widths), ref)
+
+
+# ------------------------------------------------------------------ 4-bit base weights
+def q4_grid(seed, N, K):
+    """Random codes, zero points and power-of-two scales: every dequantized weight is exact in bf16."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    codes = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    zeros = g.integers(0, 16, size=(N, K // 128)).astype(np.uint32)
+    scales = np.ldexp(1.0, g.integers(-5, 0, size=(N, K // 128))).astype(np.float32)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    params = (synth.f32_to_bf16_bits(scales).astype(np.uint32) | (zeros << 16)).T.copy()
+    return packed, params
+
+
+def run_q4(p, packed, params, dtype="bf16", slices=None):
+    import torch
+    X, _, A, B = to_device(p)
+    Wq = torch.from_numpy(np.ascontiguousarray(packed)).to("cuda")
+    Wp = torch.from_numpy(np.ascontiguousarray(params).view(np.int32)).to("cuda")
+    y = bd.lora_proj_q4(X, list(p.seg_starts), list(p.seg_adapter), Wq, Wp, A, B, p.scale, dtype=dtype,
+                        slices=slices)
+    torch.cuda.synchronize()
+    return y
+
+
+Q4_CASES = {
+    "prefill": dict(M=300, N=520, K=512, rank=48, seg_starts=[0, 5, 130, 131, 300], seg_adapter=[-1, 0, -1, 1]),
+    "decode": dict(M=70, N=520, K=512, rank=48, seg_starts=[0, 30, 64, 70], seg_adapter=[1, 0, -1]),
+}
+
+
+@pytest.mark.parametrize("name", list(Q4_CASES))
+def test_q4_integer_exact(name):
+    c = Q4_CASES[name]
+    p = synth.random_problem(81, n_adapters=2, scale=[1.0, 0.5], integer=True, **c)
+    packed, params = q4_grid(82, c["N"], c["K"])
+    log(f"case q4 int {name} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    exact = lora_proj_q4_ref(p.X, p.seg_starts, p.seg_adapter, packed, params, p.A, p.B, p.scale)
+    y32 = y_to_numpy(run_q4(p, packed, params, "bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(run_q4(p, packed, params, "bf16")), gates.bf16_rne_of_f64(exact))
+
+
+@pytest.mark.parametrize("name", list(Q4_CASES))
+def test_q4_random(name):
+    """Gaussian weights through the stand-in quantizer; the kernels round each weight to bf16."""
+    c = dict(Q4_CASES[name], N=1024, K=1024, rank=64)
+    p = synth.random_problem(83, n_adapters=2, scale=[0.75, 1.0], **c)
+    packed, params, *_ = synth.quantize_q4(p.W)
+    p.name = f"q4 random {name}"
+    log(f"case {p.name}")
+    ref = lora_proj_q4_ref(p.X, p.seg_starts, p.seg_adapter, packed, params, p.A, p.B, p.scale)
+    check_bf16(p, run_q4(p, packed, params), ref)
+
+
+def test_q4_sliced_decode_and_suffix_q():
+    widths = [512, 512, 1024]
+    p = sliced_problem(84, widths, 64, M=70, K=512, seg_starts=[0, 64, 70], seg_adapter=[0, -1], scale=[1.0])
+    packed, params, *_ = synth.quantize_q4(p.W)
+    p.name = "q4 sliced decode"
+    log(f"case {p.name}")
+    ref = lora_proj_q4_ref(p.X, p.seg_starts, p.seg_adapter, packed, params, p.A, p.B, p.scale, slice_n=widths)
+    check_bf16(p, run_q4(p, packed, params, slices=widths), ref)
+    q = synth.workload_problem("suffix", proj=0)
+    packed, params, *_ = synth.quantize_q4(q.W)
+    q.name = "q4 suffix q (5120 x 5120)"
+    log(f"case {q.name}")
+    check_bf16(q, run_q4(q, packed, params), lora_proj_q4_ref(q.X, q.seg_starts, q.seg_adapter, packed, params,
+                                                             q.A, q.B, q.scale))
 
 
 # ------------------------------------------------------------------ negative controls
