@@ -91,11 +91,15 @@ def adapter_rows(seg_starts, seg_adapter):
     return int(sum(s[g + 1] - s[g] for g in range(len(seg_adapter)) if seg_adapter[g] >= 0))
 
 
-def call_work(M, Ma, N, K, r, S=1):
-    """(main-kernel flops, shrink flops, algorithmic bytes) of one call of S slices."""
+def call_work(M, Ma, N, K, r, S=1, q4=False):
+    """(main-kernel flops, shrink flops, algorithmic bytes) of one call of S slices.
+
+    With 4-bit base weights W counts as its codes (N K / 2 bytes) plus one 4-byte params word per
+    128-wide group."""
     main = 2 * M * N * K + 2 * Ma * N * r
     shrink = 2 * Ma * S * r * K
-    byts = 2 * (N * K + M * K + M * N + ((S * r * K + N * r) if Ma else 0))
+    w_bytes = N * K // 2 + N * (K // 128) * 4 if q4 else 2 * N * K
+    byts = w_bytes + 2 * (M * K + M * N + ((S * r * K + N * r) if Ma else 0))
     return main, shrink, byts
 
 
@@ -139,7 +143,9 @@ class StepRunner:
         M = layers[0][0]["X"].shape[0]
         self.M, self.Ma = M, adapter_rows(seg_starts, seg_adapter)
         self.seg_starts, self.seg_adapter, self.scale = list(seg_starts), list(seg_adapter), scale
-        ws = max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, 1, "bf16", len(p.get("slices", [0])))
+        ws = max(bd.q4_workspace_bytes(M, p["N"], p["K"], synth.RANK, 1, "bf16", len(p.get("slices", [0])))
+                 if "Wq" in p else
+                 bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, 1, "bf16", len(p.get("slices", [0])))
                  for p in layers[0])
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)   # counter area starts at zero
         self.outs = {}
@@ -154,13 +160,21 @@ class StepRunner:
     def work(self):
         main = shrink = byts = 0
         for p in self.calls:
-            a, b, c = call_work(self.M, self.Ma, p["N"], p["K"], synth.RANK, len(p.get("slices", [0])))
+            a, b, c = call_work(self.M, self.Ma, p["N"], p["K"], synth.RANK, len(p.get("slices", [0])), "Wq" in p)
             main, shrink, byts = main + a, shrink + b, byts + c
         return main, shrink, byts
 
     def step(self, events=None):
         ws = self.workspace
         for i, p in enumerate(self.calls):
+            if "Wq" in p:
+                st = bd.lora_proj_q4_raw(p["X"].data_ptr(), self.seg_starts, self.seg_adapter, p["Wq"].data_ptr(),
+                                         p["Wp"].data_ptr(), [p["A"].data_ptr()], [p["B"].data_ptr()], synth.RANK,
+                                         self.scale, self.outs[(p["N"],)].data_ptr(), self.M, p["N"], p["K"], "bf16",
+                                         ws.data_ptr(), ws.numel(), self.stream, p.get("slices"))
+                if st != bd.LORA_OK:
+                    raise bd.LoraError(st, bd.status_string(st))
+                continue
             st = bd.lora_proj_raw(p["X"].data_ptr(), self.seg_starts, self.seg_adapter, p["W"].data_ptr(),
                                   [p["A"].data_ptr()], [p["B"].data_ptr()], synth.RANK, self.scale,
                                   self.outs[(p["N"],)].data_ptr(), self.M, p["N"], p["K"], "bf16",
@@ -264,15 +278,20 @@ def run_prefill(a, dev, hip, name="prefill16k"):
     return dict(value=value, ms_per_step=ms_per_step, flops=step_flops, bytes=byts, roofline=roofline)
 
 
-def run_decode(a, dev, hip, grouped=False):
+def run_decode(a, dev, hip, grouped=False, q4=False):
     import torch
     w5 = synth.WORKLOADS["suffix"]
-    tag = "suffix grouped" if grouped else "suffix"
+    tag = ("suffix q4" if q4 else "suffix") + (" grouped" if grouped else "")
     log(f"{tag}: drawing 24 layers on the device")
     layers = []
     for l in range(w5["layers"]):
         projs = device_layer(w5["cfg"], l, w5["M"], dev)
-        layers.append(group_layer(projs) if grouped else projs)
+        calls = group_layer(projs) if grouped else projs
+        if q4:
+            for p in calls:
+                p["Wq"], p["Wp"] = synth.device_quantize_q4(p["W"])
+                del p["W"]
+        layers.append(calls)
     runner = StepRunner(layers, w5["seg_starts"], w5["seg_adapter"], w5["scale"], dev)
     dmain, dshrink, dbytes = runner.work()
     wall5, _ = time_steps(runner, a.decode_steps, a.warmup, hip, events=False)
@@ -285,6 +304,8 @@ def run_decode(a, dev, hip, grouped=False):
     if grouped:
         workload = ("suffix, grouped: 24 layers x (q/k/v sliced, o, gate/up sliced, down), "
                     "64 adapter rows + 6 base-only decode rows, r=256")
+        if q4:
+            workload += "; base weights 4-bit (groups of 128, bf16 scale + zero point), adapter bf16"
     else:
         workload = "suffix: 24 layers x 7 projections, 64 adapter rows + 6 base-only decode rows, r=256"
     return dict(workload=workload,
@@ -304,7 +325,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
-    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped"), default="all",
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped", "decode_q4"),
+                    default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="run a plain device copy of MIB mebibytes (reads MIB, writes MIB) five times and exit; "
@@ -346,6 +368,8 @@ def main(argv=None):
     decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
     grouped = (run_decode(a, dev, hip, grouped=True)
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
+    q4 = (run_decode(a, dev, hip, grouped=True, q4=True)
+          if a.only in ("all", "decode", "decode_q4") and not a.no_decode else None)
     hip.close()
 
     cpu = None
@@ -364,7 +388,7 @@ def main(argv=None):
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
                roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
-               prefill_9b=pre9)
+               prefill_9b=pre9, decode_q4_grouped=q4)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -313,3 +313,24 @@ def quantize_q4(W: np.ndarray):
     packed = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
     params = (s_bits.astype(np.uint32) | (z.astype(np.uint32) << 16)).T.copy()
     return packed, params, q, s.astype(np.float32), z
+
+
+def device_quantize_q4(W):
+    """quantize_q4's recipe on a bf16 CUDA tensor (N, K), for the multi-gigabyte weight stacks the
+    benchmark times.  Returns (packed uint8 (N, K/2), params int32 (K/128, N)) on the device."""
+    import torch
+    N, K = W.shape
+    G = K // Q4_GROUP
+    Wg = W.float().view(N, G, Q4_GROUP)
+    lo = Wg.amin(dim=2).clamp(max=0.0)
+    hi = Wg.amax(dim=2).clamp(min=0.0)
+    step = (hi - lo) / 15.0
+    step = torch.where(step == 0, torch.ones_like(step), step)
+    s_b = step.to(torch.bfloat16)
+    s = s_b.float()
+    z = torch.clamp(torch.round(-lo / s), 0, 15)
+    q = torch.clamp(torch.round(Wg / s[..., None] + z[..., None]), 0, 15).to(torch.uint8).view(N, K)
+    packed = (q[:, 0::2] | (q[:, 1::2] << 4)).contiguous()
+    s_bits = s_b.view(torch.int16).to(torch.int32) & 0xFFFF
+    params = (s_bits | (z.to(torch.int32) << 16)).t().contiguous()
+    return packed, params
