@@ -11,3 +11,4 @@ rational and exact integer results, a one-hot closed form, and invariances.
 """
 from .lora_ref import (dequantize_q4, lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref,  # noqa: F401
                        validate_segments)
+from .extract_ref import extract_ref  # noqa: F401,E402
