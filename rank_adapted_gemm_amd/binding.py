@@ -23,7 +23,7 @@ MAX_SLICES, SLICE_ALIGN = 4, 256
 WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
 EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_q4",
            "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
-           "lora_proj_path", "lora_status_string")
+           "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes")
 
 _lib = None
 
@@ -66,6 +66,10 @@ def load():
     lib.lora_proj_q4.restype = ctypes.c_int
     lib.lora_proj_q4_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_int]
     lib.lora_proj_q4_workspace_bytes.restype = sz
+    lib.lora_extract.argtypes = [vp, vp, i64, i64, vp, i32, i32, i32, vp, vp, vp, vp, sz, vp]
+    lib.lora_extract.restype = ctypes.c_int
+    lib.lora_extract_workspace_bytes.argtypes = [i64, i64, i32, i32]
+    lib.lora_extract_workspace_bytes.restype = sz
     lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -147,6 +151,42 @@ def lora_proj_q4(X, seg_starts, seg_adapter, Wq, Wp, A, B, scale, out=None, work
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return out
+
+
+def extract_workspace_bytes(N: int, K: int, l: int, rank: int) -> int:
+    return int(load().lora_extract_workspace_bytes(N, K, l, rank))
+
+
+def extract_raw(Wa, Wb, N, K, omega, l, rank, power_iters, B, A, sigma, workspace, workspace_bytes_, stream=None):
+    """lora_extract with raw device addresses (ints).  Returns the status code."""
+    return int(load().lora_extract(Wa, Wb, int(N), int(K), omega, int(l), int(rank), int(power_iters), B, A, sigma,
+                                   workspace, int(workspace_bytes_), stream))
+
+
+def extract(W_adapted, W_base, rank, omega, power_iters=2, stream=None):
+    """(B (N, r), A (r, K), sigma (r,)) fp32 CUDA tensors: the rank-r truncated SVD of
+    W_adapted - W_base (bf16 CUDA tensors, N x K), with omega the K x l fp32 Gaussian test matrix."""
+    import torch
+    N, K = W_adapted.shape
+    l = omega.shape[1]
+    for t in (W_adapted, W_base):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
+            raise ValueError("weights must be contiguous bfloat16 CUDA tensors")
+    if omega.dtype != torch.float32 or not omega.is_contiguous() or omega.shape[0] != K:
+        raise ValueError("omega must be a contiguous float32 K x l tensor")
+    dev = W_adapted.device
+    B = torch.empty((N, rank), dtype=torch.float32, device=dev)
+    A = torch.empty((rank, K), dtype=torch.float32, device=dev)
+    sigma = torch.empty((rank,), dtype=torch.float32, device=dev)
+    need = extract_workspace_bytes(N, K, l, rank)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    if stream is None:
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    st = extract_raw(W_adapted.data_ptr(), W_base.data_ptr(), N, K, omega.data_ptr(), l, rank, power_iters,
+                     B.data_ptr(), A.data_ptr(), sigma.data_ptr(), ws.data_ptr(), need, stream)
+    if st != LORA_OK:
+        raise LoraError(st, status_string(st))
+    return B, A, sigma
 
 
 def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:

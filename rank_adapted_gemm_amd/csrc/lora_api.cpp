@@ -11,6 +11,7 @@
 
 #include <algorithm>
 
+#include "lora_extract.h"
 #include "lora_internal.h"
 
 namespace {
@@ -437,6 +438,53 @@ lora_status lora_proj_sliced(const void* X,
   if (n_adapters > 0 && !scales) return LORA_EINVAL;
   return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, n_slices, slice_n, Y,
                   M, N, K, dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+bool extract_args_ok(int64_t N, int64_t K, int32_t l, int32_t rank, int32_t power_iters) {
+  return N >= 1 && K >= 1 && rank >= 1 && l >= rank && l <= 512 && l % 2 == 0 && l <= std::min(N, K) &&
+         power_iters >= 0 && power_iters <= 8 && N * K * 4 < (int64_t(1) << 36);
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t lora_extract_workspace_bytes(int64_t N, int64_t K, int32_t l, int32_t rank) {
+  if (!extract_args_ok(N, K, l, rank, 0)) return 0;
+  return lora::extract_workspace_bytes(N, K, l, rank);
+}
+
+lora_status lora_extract(const void* W_adapted, const void* W_base, int64_t N, int64_t K,
+                         const float* omega, int32_t l, int32_t rank, int32_t power_iters,
+                         float* B, float* A, float* sigma,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (N < 1 || K < 1) return LORA_EINVAL;
+  if (!extract_args_ok(N, K, l, rank, power_iters)) return LORA_EUNSUPPORTED;
+  const void* ptrs[] = {W_adapted, W_base, omega, B, A, sigma};
+  for (const void* p : ptrs)
+    if (!p || !aligned16(p)) return LORA_EINVAL;
+  const size_t need = lora::extract_workspace_bytes(N, K, l, rank);
+  if (!workspace || workspace_bytes < need) return LORA_EWORKSPACE;
+  if (!aligned16(workspace)) return LORA_EINVAL;
+  const size_t w = size_t(N) * size_t(K) * 2;
+  const size_t outs[] = {size_t(N) * size_t(rank) * 4, size_t(rank) * size_t(K) * 4, size_t(rank) * 4};
+  const void* out_ptrs[] = {B, A, sigma};
+  const void* in_ptrs[] = {W_adapted, W_base, omega};
+  const size_t ins[] = {w, w, size_t(K) * size_t(l) * 4};
+  for (int i = 0; i < 3; ++i) {
+    if (overlaps(workspace, need, in_ptrs[i], ins[i]) || overlaps(workspace, need, out_ptrs[i], outs[i]))
+      return LORA_EINVAL;
+    for (int j = 0; j < 3; ++j)
+      if (overlaps(out_ptrs[i], outs[i], in_ptrs[j], ins[j]) || (i != j && overlaps(out_ptrs[i], outs[i], out_ptrs[j], outs[j])))
+        return LORA_EINVAL;
+  }
+  const hipError_t e = lora::launch_extract(W_adapted, W_base, N, K, omega, l, rank, power_iters, B, A, sigma,
+                                            workspace, stream);
+  return e == hipSuccess ? LORA_OK : LORA_EHIP;
 }
 
 }  // extern "C"

@@ -118,6 +118,11 @@ hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bo
                          hipEvent_t ev_start, hipEvent_t ev_stop);
 // 4-bit weights: dequantize codes + params (N x K) into bf16 W (prefill path).
 hipError_t launch_q4_dequant(const void* codes, const void* params, void* w, int64_t N, int64_t K, hipStream_t stream);
+// Adapter extraction (lora_extract.hip).
+size_t extract_workspace_bytes(int64_t N, int64_t K, int64_t l, int64_t r);
+hipError_t launch_extract(const void* w_adapted, const void* w_base, int64_t N, int64_t K, const float* omega,
+                          int l, int r, int power_iters, float* b_out, float* a_out, float* sigma_out,
+                          void* workspace, hipStream_t s);
 hipError_t launch_f32_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
                              hipStream_t stream);
 hipError_t launch_f32_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at,

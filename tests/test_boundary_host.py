@@ -220,3 +220,26 @@ def test_q4_workspace_query():
     assert bd.q4_workspace_bytes(70, 5120, 5120, 256) == bd.workspace_bytes(70, 5120, 5120, 256)
     assert bd.q4_workspace_bytes(70, 5120, 5000, 256) == 0
     assert bd.q4_workspace_bytes(70, 5120, 5120, 256, 1, "f32") == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(l=47), bd.LORA_EUNSUPPORTED),                 # odd l
+    (dict(rank=64), bd.LORA_EUNSUPPORTED),              # rank > l
+    (dict(l=514, rank=16), bd.LORA_EUNSUPPORTED),       # l > 512
+    (dict(power_iters=9), bd.LORA_EUNSUPPORTED),
+    (dict(Wa=None), bd.LORA_EINVAL),
+    (dict(B=FAKE5 + 4), bd.LORA_EINVAL),                # misaligned
+    (dict(workspace_bytes_=1024), bd.LORA_EWORKSPACE),
+    (dict(B=FAKE), bd.LORA_EINVAL),                     # B overlaps W_adapted
+])
+def test_extract_rejected_before_launch(kw, code):
+    a = dict(Wa=FAKE, Wb=FAKE2, N=256, K=512, omega=FAKE3, l=48, rank=32, power_iters=2, B=FAKE5,
+             A=FAKE5 + (1 << 20), sigma=FAKE5 + (2 << 20), workspace=FAKE * 512, workspace_bytes_=1 << 26)
+    a.update(kw)
+    assert bd.extract_raw(a["Wa"], a["Wb"], a["N"], a["K"], a["omega"], a["l"], a["rank"], a["power_iters"],
+                          a["B"], a["A"], a["sigma"], a["workspace"], a["workspace_bytes_"]) == code
+
+
+def test_extract_workspace_query():
+    assert bd.extract_workspace_bytes(5120, 5120, 272, 256) > 5120 * 5120 * 4
+    assert bd.extract_workspace_bytes(5120, 5120, 271, 256) == 0
