@@ -315,6 +315,39 @@ def run_decode(a, dev, hip, grouped=False, q4=False):
                 calls_per_step=n_calls, call_avg_us=round(ms5 * 1e3 / n_calls, 2))
 
 
+def run_extract(a, dev):
+    """Adapter extraction (lora_extract) from a planted rank-256 change of one q-shaped and one
+    down-shaped matrix: ms per matrix, with the change's recovery error as a check."""
+    import torch
+    out = {}
+    for name, N, K in (("q", 5120, 5120), ("down", 5120, 17408)):
+        g = torch.Generator(device=dev)
+        g.manual_seed(7_000_000 + N + K)
+        Wb = (torch.randn((N, K), generator=g, device=dev) * 0.14).to(torch.bfloat16)
+        B0 = torch.randn((N, synth.RANK), generator=g, device=dev) * 0.1
+        A0 = torch.randn((synth.RANK, K), generator=g, device=dev) * 0.1
+        Wa = (Wb.float() + B0 @ A0).to(torch.bfloat16)
+        del B0, A0
+        l = synth.RANK + 16
+        omega = torch.randn((K, l), generator=g, device=dev)
+        bd.extract(Wa, Wb, synth.RANK, omega)          # warmup
+        torch.cuda.synchronize()
+        reps = 5
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            B, A, s = bd.extract(Wa, Wb, synth.RANK, omega)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / reps
+        D = Wa.float() - Wb.float()
+        err = float(torch.linalg.norm(B @ A - D) / torch.linalg.norm(D))
+        log(f"extract {name} {N}x{K}: {ms:.1f} ms per matrix, |BA - D| / |D| = {err:.2e}")
+        out[name] = dict(N=N, K=K, rank=synth.RANK, l=l, power_iters=2, ms=round(ms, 2), rel_residual=err)
+        del Wa, Wb, omega, B, A, s, D
+        torch.cuda.empty_cache()
+    return dict(workload="extract: rank-256 factors of a planted change (bf16 weights), l=272, 2 power iterations",
+                **out)
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -325,7 +358,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
-    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped", "decode_q4"),
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped", "decode_q4",
+                                       "extract"),
                     default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -370,6 +404,7 @@ def main(argv=None):
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
     q4 = (run_decode(a, dev, hip, grouped=True, q4=True)
           if a.only in ("all", "decode", "decode_q4") and not a.no_decode else None)
+    extract = run_extract(a, dev) if a.only in ("all", "extract") else None
     hip.close()
 
     cpu = None
@@ -388,7 +423,7 @@ def main(argv=None):
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
                roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
-               prefill_9b=pre9, decode_q4_grouped=q4)
+               prefill_9b=pre9, decode_q4_grouped=q4, extract=extract)
     print(json.dumps(out), flush=True)
     return 0
 
