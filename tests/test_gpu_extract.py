@@ -65,3 +65,38 @@ def test_extract_rank_one_exact_direction():
     P = (B.double() @ A.double()).cpu().numpy()
     assert abs(float(s[0]) - np.linalg.norm(a) * np.linalg.norm(b)) <= 1e-5 * np.linalg.norm(a) * np.linalg.norm(b)
     assert np.linalg.norm(P - np.outer(a, b)) <= 1e-5 * np.linalg.norm(np.outer(a, b))
+
+
+def _int_low_rank(seed, N, K, true_rank):
+    """W_adapted = an integer rank-`true_rank` product (entries up to 45, exact in bf16), W_base = 0."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    B0 = g.integers(-3, 4, size=(N, true_rank)).astype(np.float32)
+    A0 = g.integers(-3, 4, size=(true_rank, K)).astype(np.float32)
+    D = B0 @ A0
+    assert np.abs(D).max() <= 256
+    return synth.f32_to_bf16_bits(D), synth.f32_to_bf16_bits(np.zeros_like(D)), D.astype(np.float64)
+
+
+@pytest.mark.parametrize("N,K,true_rank,r,l,iters", [
+    (300, 200, 5, 8, 16, 2),      # rank below r: the extra directions come back with zero singular values
+    (130, 72, 16, 16, 16, 0),     # no oversampling, no power iteration, ragged tiles (130 rows: a 2-row tail)
+    (72, 130, 16, 16, 18, 1),     # N < K, ragged
+])
+def test_extract_exact_low_rank(N, K, true_rank, r, l, iters):
+    import torch
+    wa, wb, D = _int_low_rank(94 + N, N, K, true_rank)
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    omega = np.random.Generator(np.random.PCG64(95)).standard_normal((K, l), dtype=np.float32)
+    log(f"case extract exact low rank N={N} K={K} true_rank={true_rank} r={r} l={l} iters={iters}")
+    B, A, s = bd.extract(dev(wa), dev(wb), r, torch.from_numpy(omega).to("cuda"), power_iters=iters)
+    torch.cuda.synchronize()
+    B, A, s = (t.double().cpu().numpy() for t in (B, A, s))
+    _, _, so = extract_ref(D, np.zeros_like(D), min(r, true_rank))
+    err = np.linalg.norm(B @ A - D) / np.linalg.norm(D)
+    kept = min(r, true_rank)
+    serr = np.max(np.abs(s[:kept] - so) / so)
+    tail = np.max(s[kept:]) / s[0] if r > kept else 0.0
+    log(f"  product err {err:.2e}  sigma err {serr:.2e}  tail {tail:.2e}")
+    assert np.all(np.isfinite(B)) and np.all(np.isfinite(A))
+    assert err <= 1e-5 and serr <= 1e-5 and tail <= 1e-5
+    assert np.all(np.diff(s) <= 0)
