@@ -348,6 +348,59 @@ def run_extract(a, dev):
                 **out)
 
 
+def measure_peaks(dev):
+    """What this GPU sustains, from probes built here (lora_probe.h): dense bf16 MFMA with no memory
+    traffic, a streaming read of 4 GiB (16x the 256 MB MALL, so it comes from HBM), and torch's copy
+    of 2 GiB (read + written bytes).  Best of three timed runs each."""
+    import torch
+    st = torch.cuda.current_stream(dev)
+    sink = torch.zeros(1024, dtype=torch.float32, device=dev)
+
+    def best(launch, reps=3):
+        launch()
+        torch.cuda.synchronize()
+        times = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            launch()
+            e1.record(st)
+            e1.synchronize()
+            times.append(e0.elapsed_time(e1) * 1e-3)
+        return min(times)
+
+    flop = {}
+
+    def mfma():
+        status, f = bd.probe_mfma_bf16_raw(2000, sink.data_ptr(), st.cuda_stream)
+        if status != bd.LORA_OK:
+            raise bd.LoraError(status, "lora_probe_mfma_bf16")
+        flop["f"] = f
+    t = best(mfma)
+    mfma_tflops = flop["f"] / t / 1e12
+    buf = torch.empty(4 << 30, dtype=torch.uint8, device=dev)
+    loops = 10
+
+    def read():
+        for _ in range(loops):
+            status = bd.probe_read_raw(buf.data_ptr(), buf.numel(), sink.data_ptr(), st.cuda_stream)
+            if status != bd.LORA_OK:
+                raise bd.LoraError(status, "lora_probe_read")
+    read_gbs = loops * buf.numel() / best(read) / 1e9
+    del buf
+    src = torch.empty(2 << 30, dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    copy_gbs = 2 * src.numel() / best(lambda: dst.copy_(src)) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    log(f"measured peaks: MFMA bf16 {mfma_tflops:.0f} TFLOP/s, HBM read {read_gbs:.0f} GB/s, "
+        f"copy {copy_gbs:.0f} GB/s (read + write)")
+    return dict(mfma_bf16_tflops=round(mfma_tflops, 1), hbm_read_gbs=round(read_gbs, 1),
+                hbm_copy_gbs=round(copy_gbs, 1),
+                how="probes built here: 4 independent v_mfma_f32_32x32x16_bf16 chains per wave, 16 waves per CU, "
+                    "no memory traffic; streaming 16-byte reads of 4 GiB; torch copy of 2 GiB")
+
+
 # ------------------------------------------------------------------ main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -359,7 +412,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped", "decode_q4",
-                                       "extract"),
+                                       "extract", "peaks"),
                     default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -405,7 +458,15 @@ def main(argv=None):
     q4 = (run_decode(a, dev, hip, grouped=True, q4=True)
           if a.only in ("all", "decode", "decode_q4") and not a.no_decode else None)
     extract = run_extract(a, dev) if a.only in ("all", "extract") else None
+    peaks = measure_peaks(dev) if a.only in ("all", "peaks") else None
     hip.close()
+    if peaks is not None:
+        if pre.get("roofline"):
+            pre["roofline"]["measured_peak"] = peaks["mfma_bf16_tflops"]
+            pre["roofline"]["frac_of_measured_peak"] = round(pre["roofline"]["achieved"] / peaks["mfma_bf16_tflops"], 4)
+        for d in (decode, grouped, q4):
+            if d is not None:
+                d["frac_of_measured_read"] = round(d["value"] / peaks["hbm_read_gbs"], 4)
 
     cpu = None
     if not a.no_cpu_baseline:
@@ -423,7 +484,7 @@ def main(argv=None):
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
                roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
-               prefill_9b=pre9, decode_q4_grouped=q4, extract=extract)
+               prefill_9b=pre9, decode_q4_grouped=q4, extract=extract, measured_peaks=peaks)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -23,7 +23,8 @@ MAX_SLICES, SLICE_ALIGN = 4, 256
 WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
 EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_q4",
            "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
-           "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes")
+           "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes",
+           "lora_probe_mfma_bf16", "lora_probe_read")
 
 _lib = None
 
@@ -70,6 +71,10 @@ def load():
     lib.lora_extract.restype = ctypes.c_int
     lib.lora_extract_workspace_bytes.argtypes = [i64, i64, i32, i32]
     lib.lora_extract_workspace_bytes.restype = sz
+    lib.lora_probe_mfma_bf16.argtypes = [i32, vp, ctypes.POINTER(ctypes.c_double), vp]
+    lib.lora_probe_mfma_bf16.restype = ctypes.c_int
+    lib.lora_probe_read.argtypes = [vp, sz, vp, vp]
+    lib.lora_probe_read.restype = ctypes.c_int
     lib.lora_proj_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, ctypes.c_int]
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
@@ -277,3 +282,15 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return out
+
+
+def probe_mfma_bf16_raw(iters: int, sink: int, stream=None):
+    """Launch the dense-MFMA probe (lora_probe.h).  Returns (status, flop it performs)."""
+    flop = ctypes.c_double(0.0)
+    st = int(load().lora_probe_mfma_bf16(int(iters), sink, ctypes.byref(flop), stream))
+    return st, flop.value
+
+
+def probe_read_raw(src: int, nbytes: int, sink: int, stream=None) -> int:
+    """Launch the streaming-read probe (lora_probe.h) over nbytes at src.  Returns the status."""
+    return int(load().lora_probe_read(src, int(nbytes), sink, stream))

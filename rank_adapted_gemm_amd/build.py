@@ -16,7 +16,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_NAME = "liblora_proj.so"
-SOURCES = ["lora_api.cpp", "lora_bf16.hip", "lora_decode.hip", "lora_f32.hip", "lora_q4.hip", "lora_extract.hip"]
+SOURCES = ["lora_api.cpp", "lora_bf16.hip", "lora_decode.hip", "lora_f32.hip", "lora_q4.hip", "lora_extract.hip",
+           "lora_probe.hip"]
 ARCH = "gfx950"
 
 

@@ -243,3 +243,18 @@ def test_extract_rejected_before_launch(kw, code):
 def test_extract_workspace_query():
     assert bd.extract_workspace_bytes(5120, 5120, 272, 256) > 5120 * 5120 * 4
     assert bd.extract_workspace_bytes(5120, 5120, 271, 256) == 0
+
+
+def test_probes_reject_bad_arguments():
+    """The measurement probes check their arguments on the host before any launch."""
+    st, _ = bd.probe_mfma_bf16_raw(0, FAKE)
+    assert st == bd.LORA_EINVAL
+    st, _ = bd.probe_mfma_bf16_raw(1 << 25, FAKE)
+    assert st == bd.LORA_EINVAL
+    st, _ = bd.probe_mfma_bf16_raw(10, None)
+    assert st == bd.LORA_EINVAL
+    assert bd.probe_read_raw(FAKE, 0, FAKE2) == bd.LORA_EINVAL
+    assert bd.probe_read_raw(FAKE, 24, FAKE2) == bd.LORA_EINVAL          # not a multiple of 16
+    assert bd.probe_read_raw(FAKE + 8, 32, FAKE2) == bd.LORA_EINVAL      # unaligned
+    assert bd.probe_read_raw(None, 32, FAKE2) == bd.LORA_EINVAL
+    assert bd.probe_read_raw(FAKE, 32, None) == bd.LORA_EINVAL
