@@ -27,9 +27,9 @@
  * 0..8 (else LORA_EUNSUPPORTED); N * K * 4 bytes under 2^36.  workspace: at least
  * lora_extract_workspace_bytes(N, K, l, rank) bytes of device memory, contents
  * not preserved; it must not overlap the inputs or outputs (LORA_EINVAL).
- * Asynchronous on `stream`; the caller owns every buffer.  The Cholesky and
- * eigensolver steps each run in one workgroup: an extraction of a 5120 x 5120
- * change takes about a tenth of a second on MI355X, once per weight matrix.
+ * Asynchronous on `stream`; the caller owns every buffer.  The eigensolver is
+ * one cooperative launch of 64 workgroups.  An extraction of a 5120 x 5120
+ * change takes about 20 ms on MI355X, once per weight matrix.
  */
 #ifndef LORA_EXTRACT_H
 #define LORA_EXTRACT_H
