@@ -22,17 +22,20 @@
 // with a gap after its r-th singular value.
 //
 // The products run on a tiled GEMM of arbitrary strides (LDS staging, 4 x 4
-// outputs per thread); the l x l ones split their long sums over many
-// workgroups and add the partial products in fp64.  orth() is CholeskyQR2
-// (Fukaya, Nakatsukasa, Yanagisawa and Yamamoto, 2014; Yamamoto et al.,
-// "Roundoff error analysis of the CholeskyQR2 algorithm", 2015): the fp64 Gram
-// matrix G = Y^T Y, its Cholesky factor R (one workgroup), Q = Y R^-1 (row
-// tiles in LDS), done twice.  A column of Y whose Cholesky pivot falls below
-// 1e-5 of its own length (relative, so 1e-10 on the squares) lies, to the
-// rounding of Y, in the span of the earlier ones; it becomes a zero column of Q
-// rather than an amplified rounding error, so a change of rank below l yields a
-// Q with zero columns, whose eigenvalues in step 5 are zero.  Step 5 is a cyclic
-// Jacobi eigensolver with the round-robin pairing in one workgroup, fp64.
+// outputs per thread); products with few output tiles split their long sums
+// over slabs of workgroups and add the partial products in slab order (fp64
+// for the l x l ones).  orth() is CholeskyQR (Fukaya, Nakatsukasa, Yanagisawa
+// and Yamamoto, 2014; Yamamoto et al., "Roundoff error analysis of the
+// CholeskyQR2 algorithm", 2015): the fp64 Gram matrix G = Y^T Y, its Cholesky
+// factor R (blocked, one workgroup), Q = Y R^-1 (row tiles in LDS); the range
+// that steps 4-6 use takes two passes (CholeskyQR2), the power-iteration steps
+// one.  A column of Y whose Cholesky pivot falls below 1e-5 of its own length
+// (relative, so 1e-10 on the squares) lies, to the rounding of Y, in the span
+// of the earlier ones; it becomes a zero column of Q rather than an amplified
+// rounding error, so a change of rank below l yields a Q with zero columns,
+// whose eigenvalues in step 5 are zero.  Step 5 is a cyclic Jacobi eigensolver
+// with the round-robin pairing, fp64, its rounds spread over a cooperative
+// grid.
 // Extraction runs once per weight matrix, outside the serving path.
 #include <algorithm>
 #include <cmath>
