@@ -264,7 +264,10 @@ __device__ __forceinline__ void k_loop_pingpong(f32x16 (&acc)[C::FN][C::FM], int
     wait_stages<C::PW>(min(t + D, ntiles - 1) - (t + 1));
     __syncthreads();
     __builtin_amdgcn_sched_barrier(0);
-    // ---- C(t)
+    // ---- C(t), at raised wave priority: where the two waves of a SIMD meet,
+    // the one in its multiply phase issues first (1.4% faster on the 16k
+    // projections)
+    __builtin_amdgcn_s_setprio(1);
 #pragma unroll
     for (int s = 0; s < BK / 16; ++s)
 #pragma unroll
@@ -272,6 +275,7 @@ __device__ __forceinline__ void k_loop_pingpong(f32x16 (&acc)[C::FN][C::FM], int
 #pragma unroll
         for (int j = 0; j < C::FM; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
+    __builtin_amdgcn_s_setprio(0);
     __builtin_amdgcn_sched_barrier(0);
     __syncthreads();
   }
