@@ -41,6 +41,19 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
 // the workspace's counter area.
 bool decode_counters_fit(int64_t N) { return ((N + 127) / 128 + 3) * 8 <= LORA_WORKSPACE_COUNTER_BYTES; }
 
+// Rows of each adapter and the first virtual row tile of each, for the
+// adapter-sorted shrink (the segment table is already validated).
+lora::ShrinkPlan shrink_plan(const SegTable& st, int32_t n_adapters) {
+  lora::ShrinkPlan sp{};
+  sp.n_adapters = n_adapters;
+  for (int g = 0; g < st.n; ++g)
+    if (st.adapter[g] >= 0) sp.rows[st.adapter[g]] += st.start[g + 1] - st.start[g];
+  sp.tile_off[0] = 0;
+  for (int a = 0; a < n_adapters; ++a)
+    sp.tile_off[a + 1] = sp.tile_off[a] + (sp.rows[a] + lora::kShrinkRows - 1) / lora::kShrinkRows;
+  return sp;
+}
+
 lora_status check_shape(int64_t M, int64_t N, int64_t K, lora_dtype dtype) {
   if (!dtype_ok(dtype)) return LORA_EUNSUPPORTED;
   if (M < 0 || N < 1 || K < 1) return LORA_EINVAL;
@@ -351,7 +364,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
       p.W = wcopy;
       p.w_bytes = uint32_t(size_t(N) * size_t(K) * 2);
     }
-    if (e == hipSuccess && has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, false, stream);
+    if (e == hipSuccess && has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, shrink_plan(tbl, n_adapters), stream);
     if (e == hipSuccess)
       e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, false, stream, main_start,
                                  main_stop);

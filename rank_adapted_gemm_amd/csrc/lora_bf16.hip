@@ -77,9 +77,16 @@ __device__ __forceinline__ void wait_stages(int stages) {
 
 // A wave's PW loads of a stage are consecutive 16-row groups of one side (the
 // weight rows come first and fill whole waves), so they go out in groups of up
-// to four under one M0 value.
-template <class C>
-__device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane) {
+// to four under one M0 value.  GATHER: the activation side's loads start at
+// the per-lane byte offsets gx[] (gather_offsets).  A row with no X row behind
+// it starts at kGatherMasked: past every operand (each under 2 GiB) even after
+// a load group's bias of up to 3 KiB, so it loads zeros, and with more than 128
+// rows a row of X is under 17 MB, so adding the K offset cannot wrap.  (A
+// compare and select per load here cost 0.6% of a 16k call.)
+constexpr uint32_t kGatherMasked = 0x80001000u;
+template <class C, bool GATHER = false>
+__device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane,
+                                            const uint32_t* gx = nullptr) {
   static_assert((C::TN / 16) % C::PW == 0, "a wave's groups must lie on one side");
   constexpr int NG = C::PW < 4 ? C::PW : 4;
   static_assert(C::PW % NG == 0, "groups of loads must split evenly");
@@ -94,9 +101,29 @@ __device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const S
     for (int i = 0; i < NG; ++i) {
       const int r = (g0 + q + i) * 16 + (lane >> 2) - (wside ? 0 : C::TN);
       const int c = (lane & 3) ^ ((r >> 2) & 3);
-      off[i] = uint32_t(sd.row0 + r) * sd.ld_bytes + uint32_t(k0 + c * 8) * 2u;
+      if (GATHER && !wside) {
+        off[i] = gx[q + i] + uint32_t(k0) * 2u;
+      } else {
+        off[i] = uint32_t(sd.row0 + r) * sd.ld_bytes + uint32_t(k0 + c * 8) * 2u;
+      }
     }
     dma16_group<NG>(sd.res, off, base + uint32_t(g0 + q) * 1024u);
+  }
+}
+
+// The activation-side offsets of issue_stage<C, true> for this lane, from the
+// row map xrows (LDS, -1 for none): row * ld + the lane's swizzled chunk, the
+// same for every stage.  Weight-side waves get none.
+template <class C>
+__device__ __forceinline__ void gather_offsets(uint32_t (&gx)[C::PW], const int* xrows, uint32_t ld_bytes, int wave,
+                                               int lane) {
+  const int g0 = wave * C::PW;
+#pragma unroll
+  for (int i = 0; i < C::PW; ++i) {
+    const int r = (g0 + i) * 16 + (lane >> 2) - C::TN;
+    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int row = r >= 0 ? xrows[r] : -1;
+    gx[i] = row >= 0 ? uint32_t(row) * ld_bytes + uint32_t(c) * 16u : kGatherMasked;
   }
 }
 
@@ -147,9 +174,9 @@ __device__ __forceinline__ void mma_stage(f32x16 (&acc)[C::FN][C::FM], const cha
 // ring slot t % NSTAGE; the loads of stages t+1 .. t+NSTAGE-2 stay in flight
 // while stage t is consumed.  With MASK_ROWS the activation rows outside the
 // activation side's [lo, hi) enter the MFMAs as zero.
-template <class C, bool MASK_ROWS, bool TAIL, class Src>
+template <class C, bool MASK_ROWS, bool TAIL, bool GATHER, class Src>
 __device__ __forceinline__ void k_stages(f32x16 (&acc)[C::FN][C::FM], int t0, int t1, int ntiles, int kdim, Src& src,
-                                         char* smem, int wave, int lane, int wrow, int xrow) {
+                                         char* smem, int wave, int lane, int wrow, int xrow, const uint32_t* gx) {
   for (int t = t0; t < t1; ++t) {
     // stage t has landed once at most the loads of the stages issued after it remain
     wait_stages<C::PW>(min(NSTAGE - 2, ntiles - 1 - t));
@@ -158,7 +185,7 @@ __device__ __forceinline__ void k_stages(f32x16 (&acc)[C::FN][C::FM], int t0, in
       Side ws, xs;
       int k0;
       src(t + NSTAGE - 1, ws, xs, k0);
-      issue_stage<C>(smem + ((t + NSTAGE - 1) % NSTAGE) * C::STAGE, ws, xs, k0, wave, lane);
+      issue_stage<C, GATHER>(smem + ((t + NSTAGE - 1) % NSTAGE) * C::STAGE, ws, xs, k0, wave, lane, gx);
     }
     Side ws, xs;
     int k0;
@@ -169,23 +196,30 @@ __device__ __forceinline__ void k_stages(f32x16 (&acc)[C::FN][C::FM], int t0, in
   }
 }
 
-template <class C, bool MASK_ROWS, class Src>
+template <class C, bool MASK_ROWS, bool GATHER = false, class Src>
 __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, int ntail, int kdim, Src src,
-                                       char* smem, int tid, int wn, int wm) {
+                                       char* smem, int tid, int wn, int wm, const int* xrows = nullptr) {
   if (ntiles <= 0) return;
   const int lane = tid & 63, wave = tid >> 6;
   const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
+  uint32_t gx[C::PW] = {};
+  if constexpr (GATHER) {
+    Side ws, xs;
+    int k0;
+    src(0, ws, xs, k0);
+    gather_offsets<C>(gx, xrows, xs.ld_bytes, wave, lane);
+  }
 #pragma unroll
   for (int p = 0; p < NSTAGE - 1; ++p) {
     if (p < ntiles) {
       Side ws, xs;
       int k0;
       src(p, ws, xs, k0);
-      issue_stage<C>(smem + p * C::STAGE, ws, xs, k0, wave, lane);
+      issue_stage<C, GATHER>(smem + p * C::STAGE, ws, xs, k0, wave, lane, gx);
     }
   }
-  k_stages<C, MASK_ROWS, false>(acc, 0, ntail, ntiles, kdim, src, smem, wave, lane, wrow, xrow);
-  k_stages<C, MASK_ROWS, true>(acc, ntail, ntiles, ntiles, kdim, src, smem, wave, lane, wrow, xrow);
+  k_stages<C, MASK_ROWS, false, GATHER>(acc, 0, ntail, ntiles, kdim, src, smem, wave, lane, wrow, xrow, gx);
+  k_stages<C, MASK_ROWS, true, GATHER>(acc, ntail, ntiles, ntiles, kdim, src, smem, wave, lane, wrow, xrow, gx);
   __syncthreads();   // the ring is reused by whatever runs next
 }
 
@@ -302,63 +336,82 @@ __device__ __forceinline__ void tile_of_block(int b, int ntn, int ntm, int& tn, 
 }
 
 // ------------------------------------------------------------------ shrink
-// Grid: one block per (rank tile, row tile).  For every adapter segment that
-// overlaps the block's rows: acc = A_a[rank tile] X[rows]^T, then
-// T = s_a acc (s_a the scale of the segment's adapter) stored as bf16 hi and lo
-// parts on the segment's rows only.
+// Adapter-sorted: the rows that name adapter a, gathered from all its segments
+// in row order, form a virtual row range (ShrinkPlan), and the grid has one
+// block per (rank tile, virtual row tile).  A block computes
+// acc = A_a[rank tile] X[its rows]^T with the activation rows loaded through an
+// LDS row map, then stores T = s_a acc as bf16 hi and lo parts on those rows.
+// One K loop per tile whatever the batch's interleaving of adapters, and no
+// rows computed only to be dropped, except in each adapter's last tile.
 template <class C>
-__global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, AdapterTable at, int ntn, int ntm) {
+__global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, AdapterTable at, ShrinkPlan sp, int ntn,
+                                                       int ntm) {
+  static_assert(C::TM == kShrinkRows, "shrink tiles are planned in kShrinkRows rows");
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
-  int tn, tm;
-  tile_of_block(blockIdx.x, ntn, ntm, tn, tm);
-  const int j0 = tn * C::TN, m0 = tm * C::TM;
-  const int m1 = min(m0 + C::TM, p.M);
+  __shared__ int phys[C::TM];
+  int tn, tv;
+  tile_of_block(blockIdx.x, ntn, ntm, tn, tv);
+  int a = 0;                                   // the adapter whose virtual rows tile tv covers
+  while (a + 1 < sp.n_adapters && sp.tile_off[a + 1] <= tv) ++a;
+  const int v0 = (tv - sp.tile_off[a]) * C::TM, nrows = min(C::TM, sp.rows[a] - v0);
+  const int j0 = tn * C::TN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
-  const i32x4 xres = make_rsrc_words(p.X, p.x_bytes);
   const auto tres = make_rsrc(p.T, p.t_bytes);
   const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.trank) * 2u;   // T_lo follows T_hi
 
-  for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
-    const int a = st.adapter[g];
-    if (a < 0) continue;
-    const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
-    // rows of the tile outside [lo, hi) are computed but never stored
-    const Side as{make_rsrc_words(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.trank};
-    const Side xs{xres, uint32_t(p.K) * 2u, m0, lo, hi};
-    f32x16 acc[C::FN][C::FM];
+  // row of X behind each of the tile's virtual rows: adapter a's segments in
+  // row order, concatenated (-1 past its last row)
+  for (int r = tid; r < C::TM; r += C::NT) {
+    int row = -1;
+    if (r < nrows) {
+      int v = v0 + r;
+      for (int g = 0; g < st.n; ++g) {
+        if (st.adapter[g] != a) continue;
+        const int len = st.start[g + 1] - st.start[g];
+        if (v < len) {
+          row = st.start[g] + v;
+          break;
+        }
+        v -= len;
+      }
+    }
+    phys[r] = row;
+  }
+  __syncthreads();
+
+  const Side as{make_rsrc_words(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.trank};
+  const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, 0, 0, 0};
+  f32x16 acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+  const int nk = (p.K + BK - 1) / BK;
+  k_loop<C, false, true>(acc, nk, p.K / BK, p.K,
+                         [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = t * BK; },
+                         smem, tid, wn, wm, phys);
+  // acc[i][j][r]: rank index j0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+  //               virtual row wm*(TM/WM) + j*32 + lane%32 of the tile
+#pragma unroll
+  for (int j = 0; j < C::FM; ++j) {
+    const int row = phys[wm * (C::TM / C::WM) + j * 32 + (lane & 31)];
 #pragma unroll
     for (int i = 0; i < C::FN; ++i)
 #pragma unroll
-      for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
-    const int nk = (p.K + BK - 1) / BK;
-    k_loop<C, false>(acc, nk, p.K / BK, p.K,
-              [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = t * BK; },
-              smem, tid, wn, wm);
-    // acc[i][j][r]: rank index j0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
-    //               row m0 + wm*(TM/WM) + j*32 + lane%32
+      for (int q = 0; q < 4; ++q) {
+        const int jr = j0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
+        float h[4], l[4];
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) {
-      const int m = m0 + wm * (C::TM / C::WM) + j * 32 + (lane & 31);
-      const bool row_ok = m >= lo && m < hi;
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int jr = j0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
-          float h[4], l[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) split_hi_lo(at.scale[a] * acc[i][j][q * 4 + e], h[e], l[e]);
-          const uint32_t off = (row_ok && jr < p.trank) ? (uint32_t(m) * uint32_t(p.trank) + uint32_t(jr)) * 2u
+        for (int e = 0; e < 4; ++e) split_hi_lo(at.scale[a] * acc[i][j][q * 4 + e], h[e], l[e]);
+        const uint32_t off = (row >= 0 && jr < p.trank) ? (uint32_t(row) * uint32_t(p.trank) + uint32_t(jr)) * 2u
                                                         : kMaskedOffset;
-          const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};
-          const u32x2 lv{pack2(l[0], l[1]), pack2(l[2], l[3])};
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), tres, off, 0, 0);
-          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, lv), tres,
-                                                off == kMaskedOffset ? kMaskedOffset : off + lo_base, 0, 0);
-        }
-    }
-    __syncthreads();   // the next segment's K-loop reuses the LDS stages
+        const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};
+        const u32x2 lv{pack2(l[0], l[1]), pack2(l[2], l[3])};
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), tres, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, lv), tres,
+                                              off == kMaskedOffset ? kMaskedOffset : off + lo_base, 0, 0);
+      }
   }
 }
 
@@ -474,16 +527,18 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
 using MainBig = Tile<256, 256, 2, 4>;
 using MainSmall = Tile<64, 64, 2, 2>;
 using ShrinkBig = Tile<128, 128, 2, 2>;
-using ShrinkSmall = Tile<64, 64, 2, 2>;
 
 template <class C>
-hipError_t launch_shrink_t(const ProjArgs& p, const SegTable& st, const AdapterTable& at, hipStream_t s) {
-  const int ntn = (p.trank + C::TN - 1) / C::TN, ntm = (p.M + C::TM - 1) / C::TM;
+hipError_t launch_shrink_t(const ProjArgs& p, const SegTable& st, const AdapterTable& at, const ShrinkPlan& sp,
+                           hipStream_t s) {
+  const int ntn = (p.trank + C::TN - 1) / C::TN, ntm = sp.tile_off[sp.n_adapters];
+  if (ntm == 0) return hipSuccess;
   ProjArgs pa = p;
   SegTable sa = st;
   AdapterTable aa = at;
+  ShrinkPlan spa = sp;
   int a0 = ntn, a1 = ntm;
-  void* args[] = {&pa, &sa, &aa, &a0, &a1};
+  void* args[] = {&pa, &sa, &aa, &spa, &a0, &a1};
   return hipLaunchKernel(reinterpret_cast<const void*>(&shrink_kernel<C>), dim3(ntn * ntm), dim3(C::NT), args, 0, s);
 }
 
@@ -502,9 +557,9 @@ hipError_t launch_main_t(const ProjArgs& p, const SegTable& st, const AdapterTab
 
 }  // namespace
 
-hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at, bool small_m,
+hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at, const ShrinkPlan& sp,
                               hipStream_t stream) {
-  return small_m ? launch_shrink_t<ShrinkSmall>(p, st, at, stream) : launch_shrink_t<ShrinkBig>(p, st, at, stream);
+  return launch_shrink_t<ShrinkBig>(p, st, at, sp, stream);
 }
 
 hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at, bool has_adapter,

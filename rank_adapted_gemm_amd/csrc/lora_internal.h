@@ -19,6 +19,18 @@ struct SegTable {
   int8_t adapter[LORA_MAX_SEGMENTS];          // -1 or adapter index
 };
 
+// Adapter-sorted shrink: the rows that name adapter a, over all its segments
+// in row order, form one virtual row range of rows[a] rows, cut into tiles of
+// kShrinkRows; tile_off[a] is the first such tile of adapter a and
+// tile_off[n_adapters] the total, so every shrink tile belongs to one adapter
+// however the batch interleaves them.
+constexpr int kShrinkRows = 128;
+struct ShrinkPlan {
+  int32_t n_adapters;
+  int32_t rows[LORA_MAX_ADAPTERS];
+  int32_t tile_off[LORA_MAX_ADAPTERS + 1];
+};
+
 struct AdapterTable {
   const void* A[LORA_MAX_ADAPTERS];           // (S r) x K each (device), S = number of slices
   const void* B[LORA_MAX_ADAPTERS];           // N x r each (device)
@@ -109,8 +121,8 @@ struct DecodePlan {
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t trank, int64_t n_used);
 
 // Launchers (return the HIP status of the launch).
-hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
-                              bool small_m, hipStream_t stream);
+hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at, const ShrinkPlan& sp,
+                              hipStream_t stream);
 hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
                             bool has_adapter, bool f32_out, bool small_m, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop);

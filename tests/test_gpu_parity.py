@@ -355,6 +355,36 @@ def test_per_adapter_scales_and_ranks_exact(name):
     assert np.array_equal(y_bits(run(p, dtype="bf16")), gates.bf16_rne_of_f64(exact))
 
 
+def interleaved_table(seed, M, n_adapters):
+    """Segments of 1..40 rows naming a random adapter or none (neighbours may repeat)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    starts, labels = [0], []
+    while starts[-1] < M:
+        starts.append(min(M, starts[-1] + int(g.integers(1, 41))))
+        labels.append(int(g.integers(-1, n_adapters)))
+    return starts, labels
+
+
+@pytest.mark.parametrize("M", [700, 2100])
+def test_interleaved_adapters_exact(M):
+    """Many short segments of four adapters (and base rows) interleaved through a prefill batch, so
+    most row tiles hold several adapters and each adapter's rows are scattered over the batch: the
+    adapter-sorted shrink gathers them.  Integer inputs, power-of-two scales: the fp32 store equals
+    the exact result and the bf16 store is its correct rounding."""
+    starts, labels = interleaved_table(40 + M, M, 4)
+    p = synth.random_problem(41, scale=[1.0, 0.5, -2.0, 0.25], integer=True, M=M, N=264, K=136, rank=48,
+                             seg_starts=starts, seg_adapter=labels, n_adapters=4)
+    p.name = f"interleaved M={M}"
+    log(f"case interleaved adapters M={M} segments={len(labels)} path={bd.path(p.M, p.N, p.K, p.rank)}")
+    assert bd.path(p.M, p.N, p.K, p.rank) == "prefill"
+    exact = lora_proj_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(run(p, dtype="bf16")), gates.bf16_rne_of_f64(exact))
+
+
 @pytest.mark.parametrize("name", list(PER_ADAPTER_CASES))
 def test_per_adapter_scales_random(name):
     """Gaussian inputs, distinct scales per adapter, bf16 gate against the oracle."""
