@@ -366,8 +366,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     }
     if (e == hipSuccess && has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, shrink_plan(tbl, n_adapters), stream);
     if (e == hipSuccess)
-      e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, false, stream, main_start,
-                                 main_stop);
+      e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
   }
   return e == hipSuccess ? LORA_OK : LORA_EHIP;
 }

@@ -439,8 +439,7 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
     const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0, 0, p.M};
     const int nk = (p.K + BK - 1) / BK;
     auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BK; };
-    if constexpr (C::NW == 8) k_loop_pingpong<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
-    else k_loop<C, false>(acc, nk, p.K / BK, p.K, src, smem, tid, wn, wm);
+    k_loop_pingpong<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
   }
 
   // expand: for each adapter segment overlapping the tile, stages alternate
@@ -460,8 +459,7 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
       const Side tl{tres, tld, lo_row0, lo + p.M, hi + p.M};
       const int nr = 2 * ((p.rank + BK - 1) / BK);
       auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
-      if constexpr (C::NW == 8) k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm);
-      else k_loop<C, true>(acc, nr, 2 * (p.rank / BK), p.rank, src, smem, tid, wn, wm);
+      k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm);
     }
   }
 
@@ -519,13 +517,12 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
   }
 }
 
-// Tile choices.  Large M: 256x256 tiles, eight waves of 128 (n) x 64 (m): two
+// Tile choices.  Output: 256x256 tiles, eight waves of 128 (n) x 64 (m): two
 // waves per SIMD, so one wave's MFMAs cover the other's LDS waits and
 // barriers; 128 fp32 accumulators per lane, 128 KiB of LDS for the ring.
-// Small M (decode batches) and the shrink: smaller tiles so enough blocks
-// exist to fill the CUs.
+// Shrink: 128x128 tiles, so a 256-wide rank still gives two blocks per row
+// tile.  (Batches of at most 128 rows take the decode kernel.)
 using MainBig = Tile<256, 256, 2, 4>;
-using MainSmall = Tile<64, 64, 2, 2>;
 using ShrinkBig = Tile<128, 128, 2, 2>;
 
 template <class C>
@@ -563,10 +560,7 @@ hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const Adapt
 }
 
 hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at, bool has_adapter,
-                            bool f32_out, bool small_m, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
-  if (small_m)
-    return f32_out ? launch_main_t<MainSmall, true>(p, st, at, has_adapter, stream, e0, e1)
-                   : launch_main_t<MainSmall, false>(p, st, at, has_adapter, stream, e0, e1);
+                            bool f32_out, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
   return f32_out ? launch_main_t<MainBig, true>(p, st, at, has_adapter, stream, e0, e1)
                  : launch_main_t<MainBig, false>(p, st, at, has_adapter, stream, e0, e1);
 }

@@ -124,7 +124,7 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t tr
 hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at, const ShrinkPlan& sp,
                               hipStream_t stream);
 hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at,
-                            bool has_adapter, bool f32_out, bool small_m, hipStream_t stream,
+                            bool has_adapter, bool f32_out, hipStream_t stream,
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop);
