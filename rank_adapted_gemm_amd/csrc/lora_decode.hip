@@ -373,15 +373,31 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     __syncthreads();
     gated = true;
   };
+  // One look at the T count, taken by every wave alike: true once T is stored.
+  // `word` is in a ring slot that no wave reads or refills before the second
+  // barrier.
+  auto try_gate = [&](int* word) __attribute__((always_inline)) {
+    if (gated) return true;
+    if (tid == 0) *word = __hip_atomic_load(cT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= u64(nAt * MT * 2);
+    __syncthreads();
+    gated = *word != 0;
+    __syncthreads();
+    return gated;
+  };
 
   // Stream units through the ring: n0 units of kind K0 from cursor c0, then
   // n1 expand units from cursor c1 (which continue the tile c0's units end in,
   // into the same accumulators).  The ring runs on across the change of kind;
-  // each of the two loops multiplies one kind, fixed at compile time.
+  // each of the two loops multiplies one kind, fixed at compile time.  If T is
+  // not stored when the first expand unit is due for fetching, the expand
+  // fetches are deferred: the W units already in the ring are multiplied
+  // meanwhile (the ring waits count only those), and after the last of them
+  // the block waits for T and issues the expand units it skipped.
   auto run = [&](auto k0c, Cur c0, int n0, Cur c1, int n1) __attribute__((always_inline)) {
     constexpr Kind K0 = decltype(k0c)::value;
     const int n = n0 + n1;
     Cur ci = c0, cc = c0;   // next unit to fetch / to multiply
+    bool deferred = false;  // expand fetches held back until the last W unit
     auto fetch = [&](int p) __attribute__((always_inline)) {   // unit p of the sequence into ring slot p % NS
       if (p < n0) {
         issue(p % G::NS, ci, K0);
@@ -395,11 +411,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     };
     auto step = [&](int i, auto kc) __attribute__((always_inline)) {   // multiply unit i (of kind kc)
       constexpr Kind K = decltype(kc)::value;
-      const int ahead = min(G::NS - 2, n - 1 - i);
+      const int ahead = min(G::NS - 2, (deferred ? n0 : n) - 1 - i);
       if (wave < G::NA) wait_ring<G::PWA, G::NS>(ahead);
       else wait_ring<G::PWB, G::NS>(ahead);
       __syncthreads();
-      if (i + G::NS - 1 < n) fetch(i + G::NS - 1);
+      const int p = i + G::NS - 1;
+      if (p < n) {
+        if (p < n0) fetch(p);
+        else if (!deferred) {
+          if (p > n0 || try_gate(reinterpret_cast<int*>(smem + (p % G::NS) * G::STAGE))) fetch(p);
+          else deferred = true;
+        }
+      }
       const char* ws = smem + (i % G::NS) * G::STAGE;
       const char* xs = ws + TR * RB;
       const int lim = K == KIND_E ? d.rank : d.K, e0 = cc.st * UK;
@@ -439,6 +462,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt)
             acc[rg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg], bx[mt], acc[rg][mt], 0, 0, 0);
+      }
+      if (deferred && i + 1 == n0) {   // the last W unit is multiplied: wait for T, issue the expand units
+        deferred = false;
+        for (int q = n0; q < min(n, i + G::NS); ++q) fetch(q);
       }
       const int key = cc.key;
       if (i + 1 == n0) cc = c1;
