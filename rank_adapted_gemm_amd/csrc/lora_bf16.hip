@@ -239,7 +239,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, 
 // only after both groups have read it.
 template <class C, bool MASK_ROWS, class Src>
 __device__ __forceinline__ void k_loop_pingpong(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src,
-                                                char* smem, int tid, int wn, int wm) {
+                                                char* smem, int tid, int wn, int wm, uint32_t keep = 0) {
   static_assert(C::NW == 8, "ping-pong needs two waves per SIMD");
   constexpr int D = NSTAGE - 1;
   if (ntiles <= 0) return;
@@ -282,12 +282,10 @@ __device__ __forceinline__ void k_loop_pingpong(f32x16 (&acc)[C::FN][C::FM], int
 #pragma unroll
         for (int j = 0; j < C::FM; ++j) fb[s][j] = bf16x8{};
       }
-      if constexpr (MASK_ROWS) {
+      if constexpr (MASK_ROWS) {   // activation row j of this lane enters only if bit j of keep is set
 #pragma unroll
-        for (int j = 0; j < C::FM; ++j) {
-          const int grow = xs.row0 + xrow + j * 32 + (lane & 31);
-          if (grow < xs.lo || grow >= xs.hi) fb[s][j] = bf16x8{};
-        }
+        for (int j = 0; j < C::FM; ++j)
+          if (!((keep >> j) & 1u)) fb[s][j] = bf16x8{};
       }
     }
     if (t + D < ntiles) {
@@ -420,12 +418,21 @@ template <class C, bool F32_OUT>
 __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, AdapterTable at, int has_adapter,
                                                      int ntn, int ntm) {
   __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
+  __shared__ int8_t row_adapter[C::TM];   // adapter named by each row of the tile, -1 for none
   int tn, tm;
   tile_of_block(blockIdx.x, ntn, ntm, tn, tm);
   const int n0 = tn * C::TN, m0 = tm * C::TM;
   const int m1 = min(m0 + C::TM, p.M);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
+  if (has_adapter) {   // before the accumulators fill: the map is read by the expand only
+    for (int t = tid; t < C::TM; t += C::NT) row_adapter[t] = -1;
+    __syncthreads();
+    for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g)
+      for (int t = tid; t < C::TM; t += C::NT)
+        if (m0 + t >= st.start[g] && m0 + t < st.start[g + 1]) row_adapter[t] = st.adapter[g];
+    __syncthreads();
+  }
 
   f32x16 acc[C::FN][C::FM];
 #pragma unroll
@@ -442,24 +449,32 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
     k_loop_pingpong<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
   }
 
-  // expand: for each adapter segment overlapping the tile, stages alternate
-  // T_hi and T_lo against the same 32-wide slab of B_a.  The tile's slice reads
-  // its own r columns of T (a tile never straddles two slices).
+  // expand: for each adapter that rows of the tile name, stages alternate
+  // T_hi and T_lo against the same 32-wide slab of B_a, with the rows that
+  // name another adapter or none masked to zero: one pass per adapter however
+  // many segments it has in the tile (each row's own adapter adds its term in
+  // one pass, the other passes add exact zeros).  The tile's slice reads its
+  // own r columns of T (a tile never straddles two slices).
   if (has_adapter) {
     const uint32_t tcol = uint32_t(slice_of(p.sl, n0) * p.rank) * 2u;
     const i32x4 tres = make_rsrc_words(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
     const uint32_t ld = uint32_t(p.rank) * 2u, tld = uint32_t(p.trank) * 2u;
     const int lo_row0 = m0 + p.M;          // T_lo rows sit M rows after T_hi rows
+    uint32_t seen = 0;                     // adapters already applied to this tile
     for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
       const int a = st.adapter[g];
-      if (a < 0) continue;
-      const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
+      if (a < 0 || ((seen >> a) & 1u)) continue;
+      seen |= 1u << a;
+      uint32_t keep = 0;                   // this lane's activation rows that name a
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j)
+        keep |= row_adapter[wm * (C::TM / C::WM) + j * 32 + (lane & 31)] == a ? 1u << j : 0u;
       const Side bs{make_rsrc_words(at.B[a], p.b_bytes), ld, n0, 0, p.N};
-      const Side th{tres, tld, m0, lo, hi};
-      const Side tl{tres, tld, lo_row0, lo + p.M, hi + p.M};
+      const Side th{tres, tld, m0, 0, 0};
+      const Side tl{tres, tld, lo_row0, 0, 0};
       const int nr = 2 * ((p.rank + BK - 1) / BK);
       auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
-      k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm);
+      k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm, keep);
     }
   }
 
