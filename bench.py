@@ -143,9 +143,10 @@ class StepRunner:
         M = layers[0][0]["X"].shape[0]
         self.M, self.Ma = M, adapter_rows(seg_starts, seg_adapter)
         self.seg_starts, self.seg_adapter, self.scale = list(seg_starts), list(seg_adapter), scale
-        ws = max(bd.q4_workspace_bytes(M, p["N"], p["K"], synth.RANK, 1, "bf16", len(p.get("slices", [0])))
+        nad = max(len(p["A"]) if isinstance(p["A"], list) else 1 for p in layers[0])
+        ws = max(bd.q4_workspace_bytes(M, p["N"], p["K"], synth.RANK, nad, "bf16", len(p.get("slices", [0])))
                  if "Wq" in p else
-                 bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, 1, "bf16", len(p.get("slices", [0])))
+                 bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, nad, "bf16", len(p.get("slices", [0])))
                  for p in layers[0])
         self.workspace = torch.zeros(ws, dtype=torch.uint8, device=dev)   # counter area starts at zero
         self.outs = {}
@@ -175,8 +176,9 @@ class StepRunner:
                 if st != bd.LORA_OK:
                     raise bd.LoraError(st, bd.status_string(st))
                 continue
+            As, Bs = (p["A"], p["B"]) if isinstance(p["A"], list) else ([p["A"]], [p["B"]])
             st = bd.lora_proj_raw(p["X"].data_ptr(), self.seg_starts, self.seg_adapter, p["W"].data_ptr(),
-                                  [p["A"].data_ptr()], [p["B"].data_ptr()], synth.RANK, self.scale,
+                                  [t.data_ptr() for t in As], [t.data_ptr() for t in Bs], synth.RANK, self.scale,
                                   self.outs[(p["N"],)].data_ptr(), self.M, p["N"], p["K"], "bf16",
                                   ws.data_ptr(), ws.numel(), self.stream,
                                   None if events is None else events[i], p.get("slices"))
@@ -276,6 +278,52 @@ def run_prefill(a, dev, hip, name="prefill16k"):
     del runner, layer
     torch.cuda.empty_cache()
     return dict(value=value, ms_per_step=ms_per_step, flops=step_flops, bytes=byts, roofline=roofline)
+
+
+MIXED_ADAPTERS = 4
+
+
+def mixed_table(M, n_adapters, seed=3):
+    """Segments of 20..140 rows, each naming one of n_adapters adapters or none (seeded)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    starts, labels = [0], []
+    while starts[-1] < M:
+        starts.append(min(M, starts[-1] + int(g.integers(20, 141))))
+        labels.append(int(g.integers(-1, n_adapters)))
+    return starts, labels
+
+
+def run_prefill_mixed(a, dev, hip):
+    """prefill16k's layer with four adapters per projection in a batch of short interleaved segments
+    (the many-adapters case): TFLOP/s of the algorithmic work, whose adapter rows are those naming any."""
+    import torch
+    w = synth.WORKLOADS["prefill16k"]
+    M = w["M"]
+    layer = device_layer(w["cfg"], 0, M, dev)
+    for pi, p in enumerate(layer):   # adapters 1..3 of each projection, drawn like adapter 0
+        p["A"] = [p["A"]] + [synth.device_normal_bf16((synth.RANK, p["K"]), synth.SIGMA_WAB,
+                                                      synth.seed_of(w["cfg"], 0, pi, synth.T_A) + 100 * j, dev)
+                             for j in range(1, MIXED_ADAPTERS)]
+        p["B"] = [p["B"]] + [synth.device_normal_bf16((p["N"], synth.RANK), synth.SIGMA_WAB,
+                                                      synth.seed_of(w["cfg"], 0, pi, synth.T_B) + 100 * j, dev)
+                             for j in range(1, MIXED_ADAPTERS)]
+    starts, labels = mixed_table(M, MIXED_ADAPTERS)
+    runner = StepRunner([layer], starts, labels, 1.0, dev)
+    main_flops, shrink_flops, _ = runner.work()
+    wall, main_ms = time_steps(runner, a.steps, a.warmup, hip)
+    ms_per_step = wall * 1e3 / a.steps
+    value = (main_flops + shrink_flops) / (ms_per_step / 1e3) / 1e12
+    main_achieved = main_flops * a.steps / (main_ms.sum() / 1e3) / 1e12
+    ma = runner.Ma
+    log(f"prefill16k_mixed: {len(labels)} segments, {ma} adapter rows: {ms_per_step:.3f} ms/step, "
+        f"{value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s")
+    del runner, layer
+    torch.cuda.empty_cache()
+    return dict(workload=f"prefill16k layer with {MIXED_ADAPTERS} adapters per projection; {M} rows in "
+                         f"{len(labels)} segments of 20-140 rows, each naming one adapter or none (seeded)",
+                value=round(value, 2), unit="TFLOP/s", ms_per_step=round(ms_per_step, 4),
+                frac=round(value / PEAK_BF16_TFLOPS, 4), main_kernel_tflops=round(main_achieved, 2),
+                adapter_rows=ma)
 
 
 def run_decode(a, dev, hip, grouped=False, q4=False):
@@ -411,8 +459,8 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
-    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "decode", "decode_grouped", "decode_q4",
-                                       "extract", "peaks"),
+    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "prefill_mixed", "decode", "decode_grouped",
+                                       "decode_q4", "extract", "peaks"),
                     default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -452,6 +500,7 @@ def main(argv=None):
                     frac=round(pre9["value"] / PEAK_BF16_TFLOPS, 4),
                     main_kernel_tflops=pre9["roofline"]["achieved"],
                     per_projection_ms=pre9["roofline"]["per_projection_ms"])
+    mixed = run_prefill_mixed(a, dev, hip) if a.only in ("all", "prefill_mixed") else None
     decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
     grouped = (run_decode(a, dev, hip, grouped=True)
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
@@ -484,7 +533,8 @@ def main(argv=None):
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
                roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
-               prefill_9b=pre9, decode_q4_grouped=q4, extract=extract, measured_peaks=peaks)
+               prefill_9b=pre9, prefill_mixed=mixed, decode_q4_grouped=q4, extract=extract,
+               measured_peaks=peaks)
     print(json.dumps(out), flush=True)
     return 0
 
