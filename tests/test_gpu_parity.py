@@ -385,6 +385,26 @@ def test_interleaved_adapters_exact(M):
     assert np.array_equal(y_bits(run(p, dtype="bf16")), gates.bf16_rne_of_f64(exact))
 
 
+def test_sorted_shrink_edge_plans():
+    """Adapter-sorted shrink plans at their edges: adapters 0 and 2 of five are named by no row (no
+    shrink tiles), adapter 1 has a single row, adapter 3 exactly 128 rows over three segments (one
+    whole virtual tile), adapter 4 129 rows (a one-row second tile).  Integer inputs, exact."""
+    starts = [0, 40, 41, 100, 150, 209, 250, 260, 339, 410]
+    labels = [-1, 1, 3, 4, 3, -1, 3, 4, -1]
+    rows = {a: sum(starts[g + 1] - starts[g] for g in range(len(labels)) if labels[g] == a) for a in range(5)}
+    assert rows == {0: 0, 1: 1, 2: 0, 3: 128, 4: 129}, rows
+    p = synth.random_problem(43, scale=[1.0, 2.0, 1.0, -0.5, 0.25], integer=True, M=410, N=136, K=72, rank=32,
+                             seg_starts=starts, seg_adapter=labels, n_adapters=5)
+    p.name = "sorted shrink edges"
+    log("case sorted shrink edge plans")
+    assert bd.path(p.M, p.N, p.K, p.rank) == "prefill"
+    exact = lora_proj_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+
+
 @pytest.mark.parametrize("name", list(PER_ADAPTER_CASES))
 def test_per_adapter_scales_random(name):
     """Gaussian inputs, distinct scales per adapter, bf16 gate against the oracle."""
