@@ -634,7 +634,7 @@ hipError_t launch_extract(const void* w_adapted, const void* w_base, int64_t N, 
   }
   if (e == hipSuccess) {
     int ll = l, sweeps = 30;
-    double tol = 1e-12;
+    double tol = 1e-10;
     void* args[] = {&cm, &cm2, &ut, &jpart, &ctr, &ll, &sweeps, &tol};
     e = hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&jacobi_kernel), dim3(kJacobiBlocks), dim3(256),
                                    args, 0, s);
