@@ -100,3 +100,21 @@ def test_extract_exact_low_rank(N, K, true_rank, r, l, iters):
     assert np.all(np.isfinite(B)) and np.all(np.isfinite(A))
     assert err <= 1e-5 and serr <= 1e-5 and tail <= 1e-5
     assert np.all(np.diff(s) <= 0)
+
+
+def test_extract_unchanged_matrix():
+    """A matrix the fine-tune left alone (W_adapted = W_base): D = 0, so the truncated SVD is zero and
+    B, A and the singular values come back exactly zero, with no NaN from the empty range."""
+    import torch
+    N, K, r, l = 200, 320, 8, 16
+    g = np.random.Generator(np.random.PCG64(96))
+    wb = synth.f32_to_bf16_bits(g.standard_normal((N, K), dtype=np.float32))
+    dev = lambda bits: torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+    omega = np.random.Generator(np.random.PCG64(97)).standard_normal((K, l), dtype=np.float32)
+    log(f"case extract unchanged matrix N={N} K={K} r={r} l={l}")
+    B, A, s = bd.extract(dev(wb), dev(wb.copy()), r, torch.from_numpy(omega).to("cuda"), power_iters=2)
+    torch.cuda.synchronize()
+    B, A, s = (t.double().cpu().numpy() for t in (B, A, s))
+    _, _, so = extract_ref(synth.bf16_bits_to_f32(wb), synth.bf16_bits_to_f32(wb), r)
+    assert np.all(so == 0)
+    assert np.all(B == 0) and np.all(A == 0) and np.all(s == 0)

@@ -103,6 +103,22 @@ def test_integer_exact(name, scale):
     assert np.array_equal(yb, gates.bf16_rne_of_f64(exact))
 
 
+@pytest.mark.parametrize("M", [32, 33, 64, 65, 80, 81, 127, 128])
+def test_decode_row_heights_exact(M):
+    """The decode kernel comes in four activation heights (M up to 32, 64, 80 and 128 rows); each
+    side of every boundary, with two adapters and base rows, integer inputs, exact."""
+    s = [0, M // 3, M // 3 + 1, M - 2, M]
+    p = synth.random_problem(31 + M, M=M, N=392, K=200, rank=48, seg_starts=s, seg_adapter=[0, -1, 1, -1],
+                             n_adapters=2, integer=True)
+    p.name = f"decode height M={M}"
+    assert bd.path(M, p.N, p.K, p.rank) == "decode"
+    log(f"case {p.name}")
+    exact = oracle(p)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(run(p, dtype="bf16")), gates.bf16_rne_of_f64(exact))
+
 # ------------------------------------------------------------------ workloads
 @pytest.fixture(scope="module")
 def layer_inputs():
