@@ -101,6 +101,19 @@ def q4_workspace_bytes(M: int, N: int, K: int, rank: int, n_adapters: int = 1, d
     return int(load().lora_proj_q4_workspace_bytes(M, N, K, rank, n_slices, n_adapters, DTYPES[dtype]))
 
 
+def _check_operands(dev, named, shapes=()):
+    """Every tensor in ``named`` (name -> tensor) on CUDA device ``dev``, and each
+    (name, tensor, shape) in ``shapes`` exactly that shape: the library reads
+    operands by pointer and sizes alone, so a mismatch here would be read out of
+    bounds on the device."""
+    for name, t in named.items():
+        if t is not None and (not t.is_cuda or t.device != dev):
+            raise ValueError(f"{name} must be a CUDA tensor on {dev}")
+    for name, t, shape in shapes:
+        if tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
 def lora_proj_q4_raw(X, seg_starts, seg_adapter, Wq, Wp, A, B, rank, scales, Y, M, N, K, dtype,
                      workspace=None, workspace_bytes_=0, stream=None, slices=None) -> int:
     """lora_proj_q4 with raw device addresses (ints); ``scales`` one float per adapter."""
@@ -143,6 +156,15 @@ def lora_proj_q4(X, seg_starts, seg_adapter, Wq, Wp, A, B, scale, out=None, work
     out_t = torch.bfloat16 if dtype == "bf16" else torch.float32
     if out is None:
         out = torch.empty((M, N), dtype=out_t, device=X.device)
+    if out.dtype != out_t or not out.is_contiguous():
+        raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
+    _check_operands(X.device, {"Wq": Wq, "Wp": Wp, "out": out, "workspace": workspace,
+                               **{f"A[{i}]": a for i, a in enumerate(A)}, **{f"B[{i}]": b for i, b in enumerate(B)}},
+                    [("Wq", Wq, (N, K // 2)), ("Wp", Wp, ((K + 127) // 128, N)), ("out", out, (M, N))]
+                    + [(f"A[{i}]", a, (n_slices * rank, K)) for i, a in enumerate(A)]
+                    + [(f"B[{i}]", b, (N, rank)) for i, b in enumerate(B)])
+    if Wq.element_size() * Wq.shape[1] != K // 2 or Wp.element_size() != 4:
+        raise ValueError("Wq holds K/2 bytes per row and Wp 32-bit words")
     need = q4_workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype, n_slices)
     if workspace is None and need:
         workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
@@ -177,9 +199,10 @@ def extract(W_adapted, W_base, rank, omega, power_iters=2, stream=None):
     for t in (W_adapted, W_base):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("weights must be contiguous bfloat16 CUDA tensors")
-    if omega.dtype != torch.float32 or not omega.is_contiguous() or omega.shape[0] != K:
+    if omega.dtype != torch.float32 or not omega.is_contiguous() or omega.dim() != 2 or omega.shape[0] != K:
         raise ValueError("omega must be a contiguous float32 K x l tensor")
     dev = W_adapted.device
+    _check_operands(dev, {"W_base": W_base, "omega": omega}, [("W_base", W_base, (N, K))])
     B = torch.empty((N, rank), dtype=torch.float32, device=dev)
     A = torch.empty((rank, K), dtype=torch.float32, device=dev)
     sigma = torch.empty((rank,), dtype=torch.float32, device=dev)
@@ -269,6 +292,11 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
         out = torch.empty((M, N), dtype=out_t, device=X.device)
     if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
         raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
+    _check_operands(X.device, {"W": W, "out": out, "workspace": workspace,
+                               **{f"A[{i}]": a for i, a in enumerate(A)}, **{f"B[{i}]": b for i, b in enumerate(B)}},
+                    [("W", W, (N, K))]
+                    + [(f"A[{i}]", a, (n_slices * rank, K)) for i, a in enumerate(A)]
+                    + [(f"B[{i}]", b, (N, rank)) for i, b in enumerate(B)])
     need = workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype, n_slices)
     if workspace is None and need:   # zero-filled: the counter area must start at zero
         workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)

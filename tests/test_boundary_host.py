@@ -258,3 +258,16 @@ def test_probes_reject_bad_arguments():
     assert bd.probe_read_raw(FAKE + 8, 32, FAKE2) == bd.LORA_EINVAL      # unaligned
     assert bd.probe_read_raw(None, 32, FAKE2) == bd.LORA_EINVAL
     assert bd.probe_read_raw(FAKE, 32, None) == bd.LORA_EINVAL
+
+
+def test_binding_rejects_host_tensors_and_wrong_shapes():
+    """The binding hands the library pointers and sizes only, so it refuses operands that are not
+    device tensors, or whose shapes disagree with the call's, before anything reaches the device."""
+    torch = pytest.importorskip("torch")
+    dev = torch.device("cuda", 0)
+    x = torch.zeros(4, 8)
+    with pytest.raises(ValueError, match="CUDA"):
+        bd._check_operands(dev, {"omega": x})
+    with pytest.raises(ValueError, match="shape"):
+        bd._check_operands(dev, {}, [("W_base", x, (4, 16))])
+    bd._check_operands(dev, {"workspace": None}, [("W", x, (4, 8))])
