@@ -118,3 +118,19 @@ def test_extract_unchanged_matrix():
     _, _, so = extract_ref(synth.bf16_bits_to_f32(wb), synth.bf16_bits_to_f32(wb), r)
     assert np.all(so == 0)
     assert np.all(B == 0) and np.all(A == 0) and np.all(s == 0)
+
+
+def test_binding_refuses_host_or_mismatched_operands():
+    """Operands the library would read by pointer and size alone: a host omega, a base matrix of the
+    wrong shape and a host output are refused before anything is launched."""
+    import torch
+    from rank_adapted_gemm_amd import binding
+    wa = torch.zeros((64, 96), dtype=torch.bfloat16, device="cuda")
+    omega = torch.zeros((96, 16), dtype=torch.float32)
+    with pytest.raises(ValueError, match="CUDA"):
+        bd.extract(wa, wa.clone(), 8, omega)
+    with pytest.raises(ValueError, match="shape"):
+        bd.extract(wa, wa[:63].contiguous(), 8, omega.cuda())
+    X = torch.zeros((4, 96), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError, match="CUDA"):
+        binding.lora_proj(X, [0, 4], [-1], wa, [], [], 1.0, out=torch.zeros((4, 64), dtype=torch.bfloat16))
