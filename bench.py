@@ -211,33 +211,92 @@ def time_steps(runner, steps, warmup, hip, events=True):
 
 
 # ------------------------------------------------------------------ CPU baseline
-def cpu_baseline(rows: int):
-    """fp64 oracle on `rows` token rows of each prefill16k projection (host recipe weights).
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    The default, 16384 rows, is the whole workload; smaller values time a row sample
-    (rows are independent, so the rate does not depend on which rows).
+
+def _host_layer(cfg, M):
+    """Host-recipe inputs of a workload's layer 0: {K: X values} and [(name, K, N, W, A, B)]."""
+    xs = {K: synth.layer_input(cfg, 0, M, K)[1] for K in sorted({K for _, K, _ in synth.PROJECTIONS})}
+    projs = []
+    for pi, (name, K, N) in enumerate(synth.PROJECTIONS):
+        (_, Wf), (_, Af), (_, Bf) = synth.projection_weights(cfg, 0, pi, K, N)
+        projs.append((name, K, N, Wf, Af, Bf))
+    return xs, projs
+
+
+def cpu_baseline(rows: int):
+    """The fp64 oracle as it stands, on the host cores, beside the GPU lines:
+
+      * prefill16k: `rows` token rows of each of the 7 projections (16,384 = the whole workload),
+        on every BLAS thread (the `value`), and 256 rows per projection on one thread;
+      * mixed (2,054 rows, 7 projections) in full;
+      * suffix (M = 70): layer 0's 7 projections in full, scaled by 24 for the stack (every layer
+        has the same shapes, so the same cost).
     """
     from oracle import lora_proj_ref
+    import threadpoolctl
+    threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
     try:
-        import threadpoolctl
-        threads = max((i.get("num_threads", 1) for i in threadpoolctl.threadpool_info()), default=1)
-    except Exception:
-        threads = os.cpu_count() or 1
+        affinity = len(os.sched_getaffinity(0))
+    except AttributeError:
+        affinity = os.cpu_count() or 1
+
+    def time_layer(xs, projs, starts, labels, M, Ma):
+        total, flops = 0.0, 0
+        for name, K, N, Wf, Af, Bf in projs:
+            X = xs[K]
+            t0 = time.perf_counter()
+            lora_proj_ref(X, starts, labels, Wf, [Af], [Bf], 1.0)
+            total += time.perf_counter() - t0
+            main, shrink, _ = call_work(M, Ma, N, K, synth.RANK)
+            flops += main + shrink
+        return total, flops
+
     g = np.random.Generator(np.random.PCG64(7))
-    total_s = 0.0
-    flops = 0
-    for pi, (name, K, N) in enumerate(synth.PROJECTIONS):
-        (_, Wf), (_, Af), (_, Bf) = synth.projection_weights(2, 0, pi, K, N)
-        Xs = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(g.standard_normal((rows, K), dtype=np.float32)))
-        t0 = time.perf_counter()
-        lora_proj_ref(Xs, [0, rows], [0], Wf, [Af], [Bf], 1.0)
-        total_s += time.perf_counter() - t0
-        main, shrink, _ = call_work(rows, rows, N, K, synth.RANK)
-        flops += main + shrink
-        log(f"  cpu oracle {name}: {rows} rows")
-    return dict(value=flops / total_s / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
+    _, projs2 = _host_layer(2, 1)   # weights of the prefill16k layer (X drawn below per sample)
+    # all threads, prefill16k rows
+    xs = {K: synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(g.standard_normal((rows, K), dtype=np.float32)))
+          for K in (5120, 17408)}
+    t_all, f_all = time_layer(xs, projs2, [0, rows], [0], rows, rows)
+    log(f"  cpu oracle prefill16k: {rows} rows x 7 projections, {f_all / 1e9:.0f} GFLOP in {t_all:.1f} s "
+        f"on {threads} threads")
+    # one thread, 256 rows
+    r1 = 256
+    xs1 = {K: v[:r1] for K, v in xs.items()}
+    with threadpoolctl.threadpool_limits(1):
+        t_one, f_one = time_layer(xs1, projs2, [0, r1], [0], r1, r1)
+    log(f"  cpu oracle prefill16k, one thread: {r1} rows x 7, {f_one / 1e9:.0f} GFLOP in {t_one:.1f} s")
+    del xs, xs1, projs2
+    # mixed and suffix in full
+    out = {}
+    for name in ("mixed", "suffix"):
+        w = synth.WORKLOADS[name]
+        xs, projs = _host_layer(w["cfg"], w["M"])
+        ma = adapter_rows(w["seg_starts"], w["seg_adapter"])
+        t, f = time_layer(xs, projs, list(w["seg_starts"]), list(w["seg_adapter"]), w["M"], ma)
+        byts = sum(call_work(w["M"], ma, N, K, synth.RANK)[2] for _, K, N, *_ in projs)
+        layers = w["layers"]
+        out[name] = dict(seconds_per_step=round(t * layers, 3), layers_timed=1, layers_per_step=layers,
+                         tflops=round(f / t / 1e12, 4), gbs=round(byts / t / 1e9, 2))
+        log(f"  cpu oracle {name}: 7 projections in full, {t:.2f} s per layer ({layers} per step)")
+        del xs, projs
+    return dict(value=f_all / t_all / 1e12, unit="TFLOP/s", cores=int(threads), kind="oracle",
                 sample=f"{rows} of 16384 rows of each of the 7 prefill16k projections, fp64 numpy oracle; "
-                       f"{flops / 1e9:.1f} GFLOP in {total_s:.1f} s")
+                       f"{f_all / 1e9:.1f} GFLOP in {t_all:.1f} s",
+                cpu_model=_cpu_model(), nproc=int(os.cpu_count() or 1), affinity_cpus=int(affinity),
+                blas_threads=int(threads),
+                one_thread=dict(value=round(f_one / t_one / 1e12, 5), unit="TFLOP/s",
+                                sample=f"{r1} rows of each of the 7 prefill16k projections on one thread"),
+                mixed_full=dict(out["mixed"], sample="all 2,054 rows of the mixed batch's 7 projections"),
+                suffix_full=dict(out["suffix"], sample="all 70 rows of the suffix batch's 7 projections of "
+                                                       "layer 0; 24 layers of the same shapes per step"))
 
 
 def traffic_record():
@@ -254,20 +313,23 @@ def traffic_record():
 
 
 # ------------------------------------------------------------------ the two timed workloads
-def run_prefill(a, dev, hip, name="prefill16k"):
+def run_prefill(a, dev, hip, name="prefill16k", steps=None, warmup=None):
     import torch
     w = synth.WORKLOADS[name]
-    log(f"{name}: drawing inputs on the device")
-    layer = device_layer(w["cfg"], 0, w["M"], dev, synth.projections(name))
-    runner = StepRunner([layer], w["seg_starts"], w["seg_adapter"], w["scale"], dev)
+    steps = a.steps if steps is None else steps
+    warmup = a.warmup if warmup is None else warmup
+    log(f"{name}: drawing {w['layers']} layer(s) on the device")
+    layers = [device_layer(w["cfg"], l, w["M"], dev, synth.projections(name)) for l in range(w["layers"])]
+    runner = StepRunner(layers, w["seg_starts"], w["seg_adapter"], w["scale"], dev)
     main_flops, shrink_flops, byts = runner.work()
-    log(f"{name}: {a.warmup} warmup + {a.steps} timed steps of {len(runner.calls)} calls")
-    wall, main_ms = time_steps(runner, a.steps, a.warmup, hip)
-    ms_per_step = wall * 1e3 / a.steps
+    log(f"{name}: {warmup} warmup + {steps} timed steps of {len(runner.calls)} calls")
+    wall, main_ms = time_steps(runner, steps, warmup, hip)
+    ms_per_step = wall * 1e3 / steps
     step_flops = main_flops + shrink_flops
     value = step_flops / (ms_per_step / 1e3) / 1e12
-    main_achieved = main_flops * a.steps / (main_ms.sum() / 1e3) / 1e12
-    per_proj_ms = main_ms.mean(axis=0)
+    main_achieved = main_flops * steps / (main_ms.sum() / 1e3) / 1e12
+    n7 = len(synth.projections(name))
+    per_proj_ms = main_ms.reshape(steps, -1, n7).mean(axis=(0, 1))   # per projection, over layers and steps
     log(f"{name}: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s; "
         + ", ".join(f"{p['name']} {t:.3f}" for p, t in zip(runner.calls, per_proj_ms)))
     roofline = dict(bound="mfma", achieved=round(main_achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
@@ -275,22 +337,14 @@ def run_prefill(a, dev, hip, name="prefill16k"):
                     kernel="main_kernel<Tile<256,256,2,4>, bf16 out>",
                     launch_avg_ms=round(float(main_ms.mean()), 4),
                     per_projection_ms={p["name"]: round(float(t), 4) for p, t in zip(runner.calls, per_proj_ms)})
-    del runner, layer
+    n_calls = len(runner.calls)
+    del runner, layers
     torch.cuda.empty_cache()
-    return dict(value=value, ms_per_step=ms_per_step, flops=step_flops, bytes=byts, roofline=roofline)
+    return dict(value=value, ms_per_step=ms_per_step, flops=step_flops, bytes=byts, roofline=roofline,
+                calls=n_calls, steps=steps)
 
 
-MIXED_ADAPTERS = 4
-
-
-def mixed_table(M, n_adapters, seed=3):
-    """Segments of 20..140 rows, each naming one of n_adapters adapters or none (seeded)."""
-    g = np.random.Generator(np.random.PCG64(seed))
-    starts, labels = [0], []
-    while starts[-1] < M:
-        starts.append(min(M, starts[-1] + int(g.integers(20, 141))))
-        labels.append(int(g.integers(-1, n_adapters)))
-    return starts, labels
+MIXED_ADAPTERS = synth.MIXED_ADAPTERS
 
 
 def run_prefill_mixed(a, dev, hip):
@@ -302,12 +356,12 @@ def run_prefill_mixed(a, dev, hip):
     layer = device_layer(w["cfg"], 0, M, dev)
     for pi, p in enumerate(layer):   # adapters 1..3 of each projection, drawn like adapter 0
         p["A"] = [p["A"]] + [synth.device_normal_bf16((synth.RANK, p["K"]), synth.SIGMA_WAB,
-                                                      synth.seed_of(w["cfg"], 0, pi, synth.T_A) + 100 * j, dev)
+                                                      synth.extra_adapter_seed(w["cfg"], 0, pi, synth.T_A, j), dev)
                              for j in range(1, MIXED_ADAPTERS)]
         p["B"] = [p["B"]] + [synth.device_normal_bf16((p["N"], synth.RANK), synth.SIGMA_WAB,
-                                                      synth.seed_of(w["cfg"], 0, pi, synth.T_B) + 100 * j, dev)
+                                                      synth.extra_adapter_seed(w["cfg"], 0, pi, synth.T_B, j), dev)
                              for j in range(1, MIXED_ADAPTERS)]
-    starts, labels = mixed_table(M, MIXED_ADAPTERS)
+    starts, labels = synth.mixed_table(M, MIXED_ADAPTERS)
     runner = StepRunner([layer], starts, labels, 1.0, dev)
     main_flops, shrink_flops, _ = runner.work()
     wall, main_ms = time_steps(runner, a.steps, a.warmup, hip)
@@ -459,7 +513,9 @@ def main(argv=None):
     ap.add_argument("--no-decode", action="store_true", help="skip the 24-layer decode stack")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
-    ap.add_argument("--only", choices=("all", "prefill", "prefill_9b", "prefill_mixed", "decode", "decode_grouped",
+    ap.add_argument("--stack-steps", type=int, default=3, help="timed passes of the 24-layer 32k stack")
+    ap.add_argument("--only", choices=("all", "prefill", "mixed", "stack32k", "prefill_9b", "prefill_mixed",
+                                       "decode", "decode_grouped",
                                        "decode_q4", "extract", "peaks"),
                     default="all",
                     help="time one workload only (for profiler runs)")
@@ -501,6 +557,25 @@ def main(argv=None):
                     main_kernel_tflops=pre9["roofline"]["achieved"],
                     per_projection_ms=pre9["roofline"]["per_projection_ms"])
     mixed = run_prefill_mixed(a, dev, hip) if a.only in ("all", "prefill_mixed") else None
+    cfg3 = run_prefill(a, dev, hip, "mixed") if a.only in ("all", "mixed") else None
+    if cfg3 is not None:
+        cfg3 = dict(workload="mixed: one adapted layer's 7 projections over 6 base-only decode rows (M=1 each) "
+                             "around one 2,048-row adapter prefill chunk (2,054 rows), rank 256",
+                    value=round(cfg3["value"], 2), unit="TFLOP/s", ms_per_step=round(cfg3["ms_per_step"], 4),
+                    frac=round(cfg3["value"] / PEAK_BF16_TFLOPS, 4), steps=cfg3["steps"],
+                    main_kernel_tflops=cfg3["roofline"]["achieved"],
+                    main_kernel_frac=cfg3["roofline"]["frac"],
+                    per_projection_ms=cfg3["roofline"]["per_projection_ms"])
+    st32 = (run_prefill(a, dev, hip, "stack32k", steps=a.stack_steps, warmup=1)
+            if a.only in ("all", "stack32k") else None)
+    if st32 is not None:
+        st32 = dict(workload="stack32k: 32,768 rows all naming the adapter through 24 adapted layers x 7 "
+                             "projections (independent weights per layer), rank 256",
+                    ms_per_pass=round(st32["ms_per_step"], 2), target_ms=416.7,
+                    value=round(st32["value"], 2), unit="TFLOP/s", frac=round(st32["value"] / PEAK_BF16_TFLOPS, 4),
+                    steps=st32["steps"], calls_per_pass=st32["calls"],
+                    main_kernel_tflops=st32["roofline"]["achieved"], main_kernel_frac=st32["roofline"]["frac"],
+                    per_projection_ms=st32["roofline"]["per_projection_ms"])
     decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
     grouped = (run_decode(a, dev, hip, grouped=True)
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
@@ -533,6 +608,7 @@ def main(argv=None):
                            M=w["M"], rank=synth.RANK, flop_per_step=pre.get("flops"), bytes_per_step=pre.get("bytes"),
                            parallelism="single GPU"),
                roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
+               mixed=cfg3, stack32k=st32,
                prefill_9b=pre9, prefill_mixed=mixed, decode_q4_grouped=q4, extract=extract,
                measured_peaks=peaks)
     print(json.dumps(out), flush=True)

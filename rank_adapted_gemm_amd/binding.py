@@ -114,6 +114,25 @@ def _check_operands(dev, named, shapes=()):
             raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
+def _stream_of(stream, dev):
+    """The torch stream a wrapper enqueues on: torch's current stream on ``dev`` when ``stream`` is
+    None, else ``stream`` itself, which must be a torch.cuda.Stream (or ExternalStream) on ``dev``.
+
+    The wrappers allocate their output and workspace inside ``torch.cuda.stream(s)``, so the
+    workspace's zero-fill is ordered before the kernel on that same stream, and the caching
+    allocator hands a freed block only to later work on that stream (which runs after the kernel).
+    Raw stream handles go through the *_raw functions, which allocate nothing."""
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream(dev)
+    if not isinstance(stream, torch.cuda.Stream):
+        raise TypeError("stream must be a torch.cuda.Stream (raw hipStream_t handles go through the *_raw "
+                        "functions, which allocate nothing)")
+    if stream.device != dev:
+        raise ValueError(f"stream is on {stream.device}, the operands on {dev}")
+    return stream
+
+
 def lora_proj_q4_raw(X, seg_starts, seg_adapter, Wq, Wp, A, B, rank, scales, Y, M, N, K, dtype,
                      workspace=None, workspace_bytes_=0, stream=None, slices=None) -> int:
     """lora_proj_q4 with raw device addresses (ints); ``scales`` one float per adapter."""
@@ -148,6 +167,7 @@ def lora_proj_q4(X, seg_starts, seg_adapter, Wq, Wp, A, B, scale, out=None, work
     for t in (X, *A, *B):
         if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous():
             raise ValueError("X, A, B must be contiguous bfloat16 CUDA tensors")
+    s = _stream_of(stream, X.device)
     for t in (Wq, Wp):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("Wq and Wp must be contiguous CUDA tensors")
@@ -155,7 +175,8 @@ def lora_proj_q4(X, seg_starts, seg_adapter, Wq, Wp, A, B, scale, out=None, work
     rank = A[0].shape[0] // n_slices if len(A) else 0
     out_t = torch.bfloat16 if dtype == "bf16" else torch.float32
     if out is None:
-        out = torch.empty((M, N), dtype=out_t, device=X.device)
+        with torch.cuda.stream(s):
+            out = torch.empty((M, N), dtype=out_t, device=X.device)
     if out.dtype != out_t or not out.is_contiguous():
         raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
     _check_operands(X.device, {"Wq": Wq, "Wp": Wp, "out": out, "workspace": workspace,
@@ -167,14 +188,13 @@ def lora_proj_q4(X, seg_starts, seg_adapter, Wq, Wp, A, B, scale, out=None, work
         raise ValueError("Wq holds K/2 bytes per row and Wp 32-bit words")
     need = q4_workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype, n_slices)
     if workspace is None and need:
-        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
+        with torch.cuda.stream(s):   # zero-filled on the call's stream: the counter area starts at zero
+            workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(X.device).cuda_stream
     st = lora_proj_q4_raw(X.data_ptr(), seg_starts, seg_adapter, Wq.data_ptr(), Wp.data_ptr(),
                           [a.data_ptr() for a in A], [b.data_ptr() for b in B], rank, scale, out.data_ptr(),
-                          M, N, K, dtype, ws_ptr, ws_bytes, stream, slices)
+                          M, N, K, dtype, ws_ptr, ws_bytes, s.cuda_stream, slices)
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return out
@@ -203,15 +223,15 @@ def extract(W_adapted, W_base, rank, omega, power_iters=2, stream=None):
         raise ValueError("omega must be a contiguous float32 K x l tensor")
     dev = W_adapted.device
     _check_operands(dev, {"W_base": W_base, "omega": omega}, [("W_base", W_base, (N, K))])
-    B = torch.empty((N, rank), dtype=torch.float32, device=dev)
-    A = torch.empty((rank, K), dtype=torch.float32, device=dev)
-    sigma = torch.empty((rank,), dtype=torch.float32, device=dev)
+    s = _stream_of(stream, dev)
     need = extract_workspace_bytes(N, K, l, rank)
-    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
-    if stream is None:
-        stream = torch.cuda.current_stream(dev).cuda_stream
+    with torch.cuda.stream(s):
+        B = torch.empty((N, rank), dtype=torch.float32, device=dev)
+        A = torch.empty((rank, K), dtype=torch.float32, device=dev)
+        sigma = torch.empty((rank,), dtype=torch.float32, device=dev)
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     st = extract_raw(W_adapted.data_ptr(), W_base.data_ptr(), N, K, omega.data_ptr(), l, rank, power_iters,
-                     B.data_ptr(), A.data_ptr(), sigma.data_ptr(), ws.data_ptr(), need, stream)
+                     B.data_ptr(), A.data_ptr(), sigma.data_ptr(), ws.data_ptr(), need, s.cuda_stream)
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return B, A, sigma
@@ -288,8 +308,10 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
     N = W.shape[0]
     n_slices = 1 if slices is None else len(slices)
     rank = A[0].shape[0] // n_slices if len(A) else 0
+    s = _stream_of(stream, X.device)
     if out is None:
-        out = torch.empty((M, N), dtype=out_t, device=X.device)
+        with torch.cuda.stream(s):
+            out = torch.empty((M, N), dtype=out_t, device=X.device)
     if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
         raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
     _check_operands(X.device, {"W": W, "out": out, "workspace": workspace,
@@ -298,15 +320,14 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
                     + [(f"A[{i}]", a, (n_slices * rank, K)) for i, a in enumerate(A)]
                     + [(f"B[{i}]", b, (N, rank)) for i, b in enumerate(B)])
     need = workspace_bytes(M, N, K, rank if len(A) else 16, len(A), dtype, n_slices)
-    if workspace is None and need:   # zero-filled: the counter area must start at zero
-        workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
+    if workspace is None and need:
+        with torch.cuda.stream(s):   # zero-filled on the call's stream: the counter area starts at zero
+            workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
     ws_ptr = workspace.data_ptr() if workspace is not None else None
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream(X.device).cuda_stream
     st = lora_proj_raw(X.data_ptr(), seg_starts, seg_adapter, W.data_ptr(),
                        [a.data_ptr() for a in A], [b.data_ptr() for b in B], rank, scale,
-                       out.data_ptr(), M, N, K, dtype, ws_ptr, ws_bytes, stream, events, slices)
+                       out.data_ptr(), M, N, K, dtype, ws_ptr, ws_bytes, s.cuda_stream, events, slices)
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return out

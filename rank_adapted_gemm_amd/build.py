@@ -6,6 +6,7 @@
 from __future__ import annotations
 
 import argparse
+import concurrent.futures
 import os
 import shutil
 import subprocess
@@ -38,19 +39,35 @@ def flags(report: bool = False) -> list[str]:
     return f
 
 
-def build(report: bool = False, verbose: bool = False) -> str:
-    out = os.path.join(PKG, LIB_NAME)
-    tmp = out + ".tmp"
-    cmd = [hipcc(), *flags(report), "-shared", "-o", tmp, *[os.path.join(CSRC, s) for s in SOURCES]]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)
-    if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{msgs}")
-    if msgs.strip() and (verbose or report):
-        print(msgs, flush=True)
+    return res.returncode, msgs
+
+
+def build(report: bool = False, verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source to an object file (in parallel, under _build/), then link the library."""
+    out = os.path.join(PKG, LIB_NAME)
+    objdir = os.path.join(ROOT, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    cmds = [[hipcc(), *flags(report), "-c", "-o", os.path.join(objdir, s + ".o"), os.path.join(CSRC, s)]
+            for s in SOURCES]
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        results = list(ex.map(lambda c: _run(c, verbose), cmds))
+    for (rc, msgs), src in zip(results, SOURCES):
+        if rc != 0:
+            raise RuntimeError(f"hipcc failed on {src} ({rc}):\n{msgs}")
+        if msgs.strip() and (verbose or report):
+            print(msgs, flush=True)
+    tmp = out + ".tmp"
+    rc, msgs = _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-o", tmp,
+                     *[os.path.join(objdir, s + ".o") for s in SOURCES]], verbose)
+    if rc != 0:
+        raise RuntimeError(f"link failed ({rc}):\n{msgs}")
     os.replace(tmp, out)
     return out
 

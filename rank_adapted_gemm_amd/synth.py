@@ -235,6 +235,26 @@ def random_problem(seed: int, M: int, N: int, K: int, rank: int, seg_starts, seg
     return p
 
 
+# ---------------------------------------------------------------- many adapters in one batch
+MIXED_ADAPTERS = 4
+
+
+def mixed_table(M: int, n_adapters: int = MIXED_ADAPTERS, seed: int = 3):
+    """Segments of 20..140 rows, each naming one of n_adapters adapters or none (seeded): the
+    many-adapters batch of the 16k-row prefill layer (212 segments at M = 16,384)."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    starts, labels = [0], []
+    while starts[-1] < M:
+        starts.append(min(M, starts[-1] + int(g.integers(20, 141))))
+        labels.append(int(g.integers(-1, n_adapters)))
+    return starts, labels
+
+
+def extra_adapter_seed(cfg: int, layer: int, proj: int, tensor: int, j: int) -> int:
+    """Seed of adapter j >= 1 of a projection in the many-adapters batch (adapter 0 uses seed_of)."""
+    return seed_of(cfg, layer, proj, tensor) + 100 * j
+
+
 # ---------------------------------------------------------------- row samples
 def sample_rows(M: int, seg_starts, n: int, seed: int, tiles=(128, 256)) -> np.ndarray:
     """Sorted distinct rows to check when the whole output is too large for the oracle.

@@ -57,6 +57,44 @@ def passes_f32(y, y_ref) -> bool:
     return rep["nonfinite"] == 0 and rep["g1"] <= F32_TOL
 
 
+def bf16_nearest_bits(y) -> np.ndarray:
+    """bf16 bits of float64 values rounded once to nearest, ties to even, without going
+    through float32 (whose own rounding could move a value across a bf16 midpoint).
+
+    The float32 route gives a candidate at most one bf16 step away; the nearest of it and its
+    two neighbours in float64 (exact: every bf16 value is a float64) is the answer.  Finite
+    nonzero values of normal bf16 range only.
+    """
+    y = np.asarray(y, dtype=np.float64)
+    f = y.astype(np.float32)
+    u = f.view(np.uint32).astype(np.uint64)
+    c = ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.int64)
+    cand = np.stack([c - 1, c, c + 1])
+    vals = (cand.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    d = np.abs(vals - y[None])
+    best = np.argmin(d, axis=0)
+    dmin = np.take_along_axis(d, best[None], 0)[0]
+    tie = (d == dmin[None]).sum(axis=0) > 1
+    pick = np.take_along_axis(cand, best[None], 0)[0]
+    if np.any(tie):   # a tie between two neighbours: the one with an even last bit
+        even = np.where(cand % 2 == 0, cand, -1)
+        pick = np.where(tie, np.max(np.where(d == dmin[None], even, -1), axis=0), pick)
+    return pick.astype(np.uint16)
+
+
+def explained_by_rounding(y, y_ref, rms_ref, slack=1e-4) -> np.ndarray:
+    """Per element: y is the correct bf16 rounding of y_ref, or y_ref lies within slack * rms of
+    the midpoint between y and that rounding (where the accumulator's own fp32 error may tip the
+    rounding either way)."""
+    y = np.asarray(y, dtype=np.float64)
+    y_ref = np.asarray(y_ref, dtype=np.float64)
+    rne = bf16_nearest_bits(y_ref)
+    rne_v = (rne.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    ok = y == rne_v
+    mid = 0.5 * (y + rne_v)
+    return ok | (np.abs(y_ref - mid) <= slack * rms_ref)
+
+
 def bf16_rne_of_f64(y) -> np.ndarray:
     """bf16 bits of the float64 values rounded once (nearest, ties to even).
 

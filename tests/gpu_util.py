@@ -1,6 +1,8 @@
 """Helpers for GPU tests: move a synthetic problem to the device, call the C-ABI, read back."""
 from __future__ import annotations
 
+import json
+import os
 import sys
 
 import numpy as np
@@ -12,6 +14,16 @@ from rank_adapted_gemm_amd import synth
 def log(msg: str):
     print(msg, flush=True)
     sys.stdout.flush()
+
+
+def record(case: str, rep: dict, past_g1: int):
+    """Append one parity result (rms, G1, G2, elements past the literal G1 bound) to the JSON-lines
+    file named by LORA_PARITY_RECORD, when set, so the figures of every large case are kept."""
+    path = os.environ.get("LORA_PARITY_RECORD")
+    if not path:
+        return
+    with open(path, "a") as f:
+        f.write(json.dumps(dict(case=case, rms=rep["rms"], g1=rep["g1"], g2=rep["g2"], past_g1=int(past_g1))) + "\n")
 
 
 def _dev_bf16(bits, torch, dev):

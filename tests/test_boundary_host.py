@@ -271,3 +271,12 @@ def test_binding_rejects_host_tensors_and_wrong_shapes():
     with pytest.raises(ValueError, match="shape"):
         bd._check_operands(dev, {}, [("W_base", x, (4, 16))])
     bd._check_operands(dev, {"workspace": None}, [("W", x, (4, 8))])
+
+
+def test_wrapper_refuses_raw_stream_handle():
+    """The tensor wrappers allocate on the stream they enqueue on, so they take torch streams only;
+    a raw handle is refused before anything reaches the device."""
+    import pytest
+    import torch
+    with pytest.raises(TypeError):
+        bd._stream_of(12345, torch.device("cuda:0"))

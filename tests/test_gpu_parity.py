@@ -14,7 +14,7 @@ import numpy as np
 import pytest
 
 import gates
-from gpu_util import log, run, to_device, y_bits, y_to_numpy
+from gpu_util import log, record, run, to_device, y_bits, y_to_numpy
 from oracle import lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref
 from rank_adapted_gemm_amd import binding as bd
 from rank_adapted_gemm_amd import synth
@@ -30,15 +30,24 @@ def oracle(p, rows=None, scale=None, seg_adapter=None):
 
 
 def check_bf16(p, y_dev, ref, rows=None, literal=True):
-    y = y_to_numpy(y_dev)
+    """G2 must hold.  With literal=True G1 must hold too; otherwise every element past the literal
+    G1 bound must be the correct bf16 rounding of the oracle value (or lie at a near-tie), so that
+    rounding alone explains it."""
+    y = y_to_numpy(y_dev) if not isinstance(y_dev, np.ndarray) else y_dev
     if rows is not None:
         y = y[rows]
     rep = gates.report(y, ref)
-    log(f"  {p.name} bf16 rms={rep['rms']:.4g} G1={rep['g1']:.3e} G2={rep['g2']:.3e}")
+    over = np.abs(y - ref) > gates.BF16_TOL * rep["rms"]
+    log(f"  {p.name} bf16 rms={rep['rms']:.4g} G1={rep['g1']:.3e} G2={rep['g2']:.3e} "
+        f"past-G1={int(over.sum())}")
+    record(p.name, rep, int(over.sum()))
     assert rep["nonfinite"] == 0
     assert rep["g2"] <= gates.BF16_TOL, rep
     if literal:
         assert rep["g1"] <= gates.BF16_TOL, rep
+    elif over.any():
+        ok = gates.explained_by_rounding(y[over], ref[over], rep["rms"])
+        assert ok.all(), f"{int((~ok).sum())} elements past G1 that rounding does not explain"
     return rep
 
 
@@ -150,13 +159,12 @@ def test_suffix_decode_full(layer_inputs, proj):
 
 @pytest.mark.parametrize("proj", range(7))
 def test_mixed_batch(layer_inputs, proj):
-    """6 base-only decode rows around a 2,048-row adapter chunk (full rows for q, sampled otherwise)."""
+    """6 base-only decode rows around a 2,048-row adapter chunk: every row and column checked."""
     p = workload(layer_inputs, "mixed", proj)
     log(f"case mixed proj={proj} path={bd.path(p.M, p.N, p.K, p.rank)}")
-    rows = None if proj == 0 else synth.sample_rows(p.M, p.seg_starts, 256, seed=proj)
-    ref = oracle(p, rows=rows)
-    check_bf16(p, run(p), ref, rows=rows)
-    check_f32out(p, run(p, dtype="bf16_f32out"), ref, rows=rows)
+    ref = oracle(p)
+    check_bf16(p, run(p), ref, literal=False)
+    check_f32out(p, run(p, dtype="bf16_f32out"), ref)
 
 
 @pytest.mark.parametrize("proj", range(7))
@@ -621,3 +629,27 @@ def test_negative_control_fails_gate(arm):
         q = synth.random_problem(17, M=300, N=520, K=256, rank=32, seg_starts=[0, 41, 300], seg_adapter=[-1, 0])
         y = run(q)
     assert not gates.passes_bf16(y_to_numpy(y), ref), arm
+
+
+# ------------------------------------------------------------------ streams
+def test_call_on_a_second_stream():
+    """The wrapper enqueues on the stream it is given: output and zero-filled workspace are
+    allocated on that stream, so the counter area's fill is ordered before the kernel even while
+    the current stream is busy, and a freed workspace is only reused by later work on it."""
+    import torch
+    side = torch.cuda.Stream()
+    for M, s, a in ((70, [0, 64, 70], [0, -1]), (300, [0, 40, 300], [-1, 0])):
+        p = synth.random_problem(90 + M, M=M, N=1000, K=520, rank=32, seg_starts=s, seg_adapter=a)
+        p.name = f"second stream M={M}"
+        log(f"case {p.name} path={bd.path(p.M, p.N, p.K, p.rank)}")
+        X, W, A, B = to_device(p)
+        torch.cuda.synchronize()
+        busy = torch.randn((4096, 4096), device="cuda")
+        outs = []
+        for _ in range(4):
+            busy = busy @ busy.t().contiguous() * 1e-3    # keeps the current stream occupied
+            outs.append(bd.lora_proj(X, s, a, W, A, B, p.scale, stream=side))   # not the current stream
+        torch.cuda.synchronize()
+        ref = oracle(p)
+        for y in outs:
+            check_bf16(p, y, ref)
