@@ -57,7 +57,8 @@ typedef enum lora_status {
   LORA_EADAPTER = 3,      /* adapter index out of range, or its A/B pointer is null */
   LORA_EUNSUPPORTED = 4,  /* shape, rank, dtype or table size outside the documented limits */
   LORA_EWORKSPACE = 5,    /* workspace missing or smaller than lora_proj_workspace_bytes() */
-  LORA_EHIP = 6           /* the HIP runtime reported an error while enqueueing */
+  LORA_EHIP = 6,          /* the HIP runtime reported an error while enqueueing */
+  LORA_EHANDOVER = 7      /* lora_workspace_status: a decode call on the workspace lost a hand-over */
 } lora_status;
 
 typedef enum lora_dtype {
@@ -103,10 +104,14 @@ typedef enum lora_dtype {
  *   workspace    device scratch of at least lora_proj_workspace_bytes(M, N, K, rank,
  *                n_adapters, dtype) bytes (may be NULL with size 0 when that is 0).  Its
  *                first LORA_WORKSPACE_COUNTER_BYTES are a counter area that the blocks of
- *                one launch use to hand work to each other: it must be all zero before the
- *                first call that uses the workspace (allocate it zero-filled), and every
- *                call leaves it zero again.  A non-zero counter area gives wrong results,
- *                never a hang.  The rest is scratch whose contents are not preserved
+ *                one decode launch (at most 128 rows) use to hand work to each other.  Every
+ *                counter carries the number of the call that last counted on it, so counts
+ *                left by earlier calls, finished or aborted, are ignored and the area never
+ *                needs clearing between calls.  Its last 8 bytes hold sticky error bits
+ *                (see lora_workspace_status), which must be zero when the workspace is
+ *                first used: allocate it zero-filled.  The rest is scratch whose contents
+ *                are not preserved.  Calls that share a workspace must not overlap in time
+ *                (order them on one stream)
  *   stream       HIP stream the work is ordered on (0 = the null stream)
  */
 lora_status lora_proj(const void* X,
@@ -285,6 +290,66 @@ const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_d
 
 /* Static description of a status code; never NULL. */
 const char* lora_status_string(lora_status s);
+
+/*
+ * lora_workspace_status — did a decode call on this workspace lose a hand-over?
+ *
+ * A decode launch (at most 128 rows) hands T = s X A^T from the blocks that
+ * compute it to the blocks that add it, and K-part sums between blocks, through
+ * counters in the workspace's counter area.  Waiting is bounded: if a block gives
+ * up waiting for T (other work held the GPU's compute units for about 0.3 s), or a
+ * count goes past its expected total, the kernel sets a sticky bit in the last 8
+ * bytes of the counter area, stores NaN in place of the output columns that
+ * depended on the hand-over, and exits.  The pages' own lesson is that a silent
+ * slow or wrong path is the failure to avoid ("serving-qwen3-8-27b-on-one-
+ * rtx-3090", Installing: a missing header made the server slower with nothing in
+ * its logs); this call is how the caller sees it.
+ *
+ *   workspace        device, a workspace passed to earlier calls (16-byte aligned)
+ *   workspace_bytes  its size, at least LORA_WORKSPACE_COUNTER_BYTES
+ *   stream           the stream those calls were ordered on
+ *
+ * Synchronizes `stream`, reads the bits, and clears them (a one-word kernel on
+ * `stream`, then a second synchronization).  Returns LORA_OK when no call since the
+ * last query lost a hand-over, LORA_EHANDOVER when one did, LORA_EINVAL for a bad
+ * argument and LORA_EHIP for a runtime error.
+ */
+lora_status lora_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * lora_debug_handover_fault — test hook for the failure path above.
+ *
+ * While `on` is non-zero, every decode call with adapter rows that is enqueued
+ * afterwards waits for one T group more than exists, with a short bounded spin,
+ * so its waits give up at once: the call's error bit is set and its output
+ * columns hold NaN, and every block still exits normally.  Process-wide; for
+ * tests only.  Returns the previous setting.
+ */
+int32_t lora_debug_handover_fault(int32_t on);
+
+/*
+ * lora_decode_plan_describe — the launch plan a decode call (1 .. 128 rows) of this
+ * shape would use, for inspection and host-side tests; nothing is launched.
+ *
+ *   M, N, K, rank, n_slices, slice_n   as in lora_proj_sliced (slice_n may be NULL
+ *                                      when n_slices == 1)
+ *   n_used                             adapters the batch's rows name (0 .. LORA_MAX_ADAPTERS)
+ *   out                                HOST, receives up to n_out values, in order:
+ *     MT                16-row activation tiles (2, 4, 5 or 8)
+ *     nst, nrs          64-wide K units per weight tile; 64-wide rank units per expand half
+ *     ntA, ntW          128-row tiles of the stacked A rows of one adapter; of W
+ *     n_used            adapters the plan is for
+ *     GA, GW            A blocks (the shrink), W blocks (stream-K over the W units)
+ *     smaxW             partial-sum slots per W tile (the most blocks sharing one tile)
+ *     off_cnt, off_pa, pa_bytes, off_pw, pw_bytes, off_th, t_bytes, off_tl, total
+ *                       workspace layout: counters, A partials, W partials, T_hi, T_lo,
+ *                       total bytes
+ *
+ * Returns the number of values the plan has (18), or 0 when the shape is not on
+ * the decode path or an argument is invalid.
+ */
+int32_t lora_decode_plan_describe(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
+                                  const int64_t* slice_n, int32_t n_used, int64_t* out, int32_t n_out);
 
 #ifdef __cplusplus
 }

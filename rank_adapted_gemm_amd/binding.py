@@ -14,9 +14,10 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "liblora_proj.so")
 
-LORA_OK, LORA_EINVAL, LORA_ESEGMENTS, LORA_EADAPTER, LORA_EUNSUPPORTED, LORA_EWORKSPACE, LORA_EHIP = range(7)
+(LORA_OK, LORA_EINVAL, LORA_ESEGMENTS, LORA_EADAPTER, LORA_EUNSUPPORTED, LORA_EWORKSPACE, LORA_EHIP,
+ LORA_EHANDOVER) = range(8)
 STATUS_NAMES = {0: "LORA_OK", 1: "LORA_EINVAL", 2: "LORA_ESEGMENTS", 3: "LORA_EADAPTER",
-                4: "LORA_EUNSUPPORTED", 5: "LORA_EWORKSPACE", 6: "LORA_EHIP"}
+                4: "LORA_EUNSUPPORTED", 5: "LORA_EWORKSPACE", 6: "LORA_EHIP", 7: "LORA_EHANDOVER"}
 DTYPES = {"bf16": 0, "f32": 1, "bf16_f32out": 2}
 MAX_SEGMENTS, MAX_ADAPTERS, MIN_RANK, MAX_RANK = 256, 32, 16, 512
 MAX_SLICES, SLICE_ALIGN = 4, 256
@@ -24,7 +25,10 @@ WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of eve
 EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_q4",
            "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
            "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes",
-           "lora_probe_mfma_bf16", "lora_probe_read")
+           "lora_probe_mfma_bf16", "lora_probe_read", "lora_workspace_status", "lora_debug_handover_fault",
+           "lora_decode_plan_describe")
+PLAN_FIELDS = ("MT", "nst", "nrs", "ntA", "ntW", "n_used", "GA", "GW", "smaxW", "off_cnt", "off_pa", "pa_bytes",
+               "off_pw", "pw_bytes", "off_th", "t_bytes", "off_tl", "total")
 
 _lib = None
 
@@ -81,6 +85,13 @@ def load():
     lib.lora_proj_path.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_workspace_status.argtypes = [vp, sz, vp]
+    lib.lora_workspace_status.restype = ctypes.c_int
+    lib.lora_debug_handover_fault.argtypes = [i32]
+    lib.lora_debug_handover_fault.restype = i32
+    lib.lora_decode_plan_describe.argtypes = [i64, i64, i64, i32, i32, ctypes.POINTER(i64), i32,
+                                              ctypes.POINTER(i64), i32]
+    lib.lora_decode_plan_describe.restype = i32
     _lib = lib
     return lib
 
@@ -343,3 +354,29 @@ def probe_mfma_bf16_raw(iters: int, sink: int, stream=None):
 def probe_read_raw(src: int, nbytes: int, sink: int, stream=None) -> int:
     """Launch the streaming-read probe (lora_probe.h) over nbytes at src.  Returns the status."""
     return int(load().lora_probe_read(src, int(nbytes), sink, stream))
+
+
+def workspace_status(workspace, stream=None) -> int:
+    """lora_workspace_status on a workspace tensor: LORA_OK, or LORA_EHANDOVER when a decode call on
+    it lost a hand-over since the last query (the bits are cleared).  Synchronizes the stream."""
+    import torch
+    s = _stream_of(stream, workspace.device)
+    return int(load().lora_workspace_status(workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                            s.cuda_stream))
+
+
+def debug_handover_fault(on: bool) -> bool:
+    """Test hook: while on, decode calls with adapter rows lose their hand-over (see the header)."""
+    return bool(load().lora_debug_handover_fault(1 if on else 0))
+
+
+def decode_plan(M: int, N: int, K: int, rank: int, n_used: int, slices=None) -> dict | None:
+    """The decode launch plan of a shape (lora_decode_plan_describe), or None off the decode path."""
+    widths = list(slices) if slices is not None else [int(N)]
+    w_arg = (ctypes.c_int64 * len(widths))(*[int(v) for v in widths])
+    out = (ctypes.c_int64 * 32)()
+    n = int(load().lora_decode_plan_describe(int(M), int(N), int(K), int(rank), len(widths), w_arg, int(n_used),
+                                             out, 32))
+    if n == 0:
+        return None
+    return dict(zip(PLAN_FIELDS, list(out[:n])))

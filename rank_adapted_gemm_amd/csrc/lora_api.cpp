@@ -10,6 +10,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "lora_extract.h"
 #include "lora_internal.h"
@@ -37,9 +38,17 @@ bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
   return a0 < b0 + nb && b0 < a0 + na;
 }
 
+// Test hook (lora_debug_handover_fault): decode calls wait for one T group more
+// than exist, with a short spin, so the failure path runs and every block exits.
+std::atomic<int> g_handover_fault{0};
+constexpr uint32_t kSpinLimit = 1u << 22;   // polls (about 0.3 s) before a wait for T gives up
+
+// Byte offset of the sticky error bits in a workspace.
+constexpr size_t kErrOffset = LORA_WORKSPACE_COUNTER_BYTES - 8;
+
 // The decode path's counters (one per 128 output columns, plus three) must fit
-// the workspace's counter area.
-bool decode_counters_fit(int64_t N) { return ((N + 127) / 128 + 3) * 8 <= LORA_WORKSPACE_COUNTER_BYTES; }
+// the workspace's counter area below the error bits.
+bool decode_counters_fit(int64_t N) { return ((N + 127) / 128 + 3) * 8 <= int64_t(kErrOffset); }
 
 // Rows of each adapter and the first virtual row tile of each, for the
 // adapter-sorted shrink (the segment table is already validated).
@@ -140,6 +149,7 @@ const char* lora_status_string(lora_status s) {
     case LORA_EUNSUPPORTED: return "shape, rank, dtype or table size outside the supported limits";
     case LORA_EWORKSPACE: return "workspace missing or too small";
     case LORA_EHIP: return "HIP runtime error while enqueueing";
+    case LORA_EHANDOVER: return "a decode call on this workspace lost a hand-over between blocks (its output holds NaN)";
   }
   return "unknown status";
 }
@@ -322,6 +332,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     d.wp_bytes = uint32_t(wp_bytes);
     d.Y = Y;
     d.cnt = reinterpret_cast<unsigned long long*>(ws + pl.off_cnt);
+    d.err = reinterpret_cast<uint32_t*>(ws + kErrOffset);
     d.PA = reinterpret_cast<float*>(ws + pl.off_pa);
     d.PW = reinterpret_cast<float*>(ws + pl.off_pw);
     d.TH = reinterpret_cast<uint16_t*>(ws + pl.off_th);
@@ -348,6 +359,8 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     d.GA = pl.GA;
     d.GW = pl.GW;
     d.smaxW = pl.smaxW;
+    d.spin_limit = kSpinLimit;
+    d.fault = g_handover_fault.load(std::memory_order_relaxed);
     for (int g = 0; g < tbl.n; ++g)
       for (int32_t m = tbl.start[g]; m < tbl.start[g + 1]; ++m)
         d.row_slot[m] = tbl.adapter[g] < 0 ? int8_t(-1) : slot_of[tbl.adapter[g]];
@@ -497,6 +510,49 @@ lora_status lora_extract(const void* W_adapted, const void* W_base, int64_t N, i
   const hipError_t e = lora::launch_extract(W_adapted, W_base, N, K, omega, l, rank, power_iters, B, A, sigma,
                                             workspace, stream);
   return e == hipSuccess ? LORA_OK : LORA_EHIP;
+}
+
+}  // extern "C"
+
+extern "C" {
+
+lora_status lora_workspace_status(void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  if (!workspace || !aligned16(workspace) || workspace_bytes < LORA_WORKSPACE_COUNTER_BYTES) return LORA_EINVAL;
+  uint32_t bits = 0;
+  if (hipMemcpyAsync(&bits, static_cast<char*>(workspace) + kErrOffset, sizeof(bits), hipMemcpyDeviceToHost,
+                     stream) != hipSuccess)
+    return LORA_EHIP;
+  if (hipStreamSynchronize(stream) != hipSuccess) return LORA_EHIP;
+  if (bits == 0) return LORA_OK;
+  // a call lost a hand-over: its counts may be anywhere, so restore the whole area
+  if (lora::launch_clear_words(static_cast<uint32_t*>(workspace), int(LORA_WORKSPACE_COUNTER_BYTES / 4), stream) !=
+          hipSuccess ||
+      hipStreamSynchronize(stream) != hipSuccess)
+    return LORA_EHIP;
+  return LORA_EHANDOVER;
+}
+
+int32_t lora_debug_handover_fault(int32_t on) { return g_handover_fault.exchange(on ? 1 : 0); }
+
+}  // extern "C"
+
+extern "C" {
+
+int32_t lora_decode_plan_describe(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_slices,
+                                  const int64_t* slice_n, int32_t n_used, int64_t* out, int32_t n_out) {
+  if (check_shape(M, N, K, LORA_BF16) != LORA_OK || M < 1 || !small_m(M) || !out) return 0;
+  if (n_used < 0 || n_used > LORA_MAX_ADAPTERS || (n_used > 0 && !rank_ok(rank))) return 0;
+  lora::Slices sl;
+  if (make_slices(n_slices, slice_n, N, sl) != LORA_OK) return 0;
+  const int64_t r = plan_rank(rank);
+  const lora::DecodePlan p = lora::decode_plan(M, N, K, r, sl.n * r, n_used);
+  const int64_t v[] = {p.MT, p.nst, p.nrs, p.ntA, p.ntW, p.n_used, p.GA, p.GW, p.smaxW,
+                       int64_t(p.off_cnt), int64_t(p.off_pa), int64_t(p.pa_bytes), int64_t(p.off_pw),
+                       int64_t(p.pw_bytes), int64_t(p.off_th), int64_t(p.t_bytes), int64_t(p.off_tl),
+                       int64_t(p.total)};
+  const int32_t n = int32_t(sizeof(v) / sizeof(v[0]));
+  for (int32_t i = 0; i < n && i < n_out; ++i) out[i] = v[i];
+  return n;
 }
 
 }  // extern "C"

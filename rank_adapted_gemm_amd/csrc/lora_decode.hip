@@ -36,6 +36,15 @@
 // atomic add, never an L2 flush.  The counters sit in the workspace's counter
 // area: zero when the workspace is first used, and put back to zero by the
 // block that uses each last, so nothing has to clear them between calls.
+//
+// Nothing fails silently ("serving-qwen3-8-27b-on-one-rtx-3090", Installing: a
+// path that silently runs wrong or slow, with nothing in the logs, is the failure
+// to avoid).  Every wait is bounded; a wait that gives up, or an arrival that
+// finds a count already at its expected total (a counter area left non-zero by a
+// call that never finished), sets a sticky bit in the last 8 bytes of the counter
+// area, which lora_workspace_status reports before it restores the area.  The
+// data a lost wait would have carried is replaced by NaN, so the outputs that
+// depended on it are NaN.
 #include <algorithm>
 #include <cmath>
 #include <type_traits>
@@ -90,9 +99,11 @@ typedef unsigned long long u64;
 
 // Arrival counters: plain device-scope adds (one round trip, no retries).  A
 // counter is zero when a call starts and the block that uses it last puts it
-// back to zero.
-__device__ inline uint32_t arrive(u64* c, uint32_t k = 1) {
-  return uint32_t(__hip_atomic_fetch_add(c, u64(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+// back to zero.  An arrival that takes a count past `total` flags the call.
+__device__ inline uint32_t arrive(u64* c, uint32_t* err, uint32_t total, uint32_t k = 1) {
+  const uint32_t old = uint32_t(__hip_atomic_fetch_add(c, u64(k), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+  if (old + k > total) __hip_atomic_fetch_or(err, kDecodeErrCount, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return old;
 }
 __device__ inline void clear(u64* c) { __hip_atomic_store(c, u64(0), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
 
@@ -139,12 +150,14 @@ __device__ inline Unit unit_of(const Cur& c, Kind kind, const DecodeArgs& d, con
 }
 
 // Spin (thread 0) until the counter reaches `want`; bounded, so a broken
-// hand-over costs time, never a hang.
-__device__ inline void wait_for(u64* c, u64 want) {
-  for (int it = 0; it < (1 << 24); ++it) {
-    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return;
+// hand-over never hangs: after `limit` polls it flags the call and returns false.
+__device__ inline bool wait_for(u64* c, u64 want, uint32_t limit, uint32_t* err) {
+  for (uint32_t it = 0; it < limit; ++it) {
+    if (__hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= want) return true;
     __builtin_amdgcn_s_sleep(2);
   }
+  __hip_atomic_fetch_or(err, kDecodeErrTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return false;
 }
 
 // Q4: the base weights come as 4-bit codes plus per-group params (see
@@ -165,6 +178,11 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   u64* const cA = d.cnt + d.ntW;                   // A blocks done
   u64* const cT = cA + 1;                          // T pieces done
   u64* const cF = cA + 2;                          // W tiles finished
+  const uint32_t t_total = uint32_t(nAt * MT * 2); // T pieces of the call
+  // the test hook waits for one piece more than exist, with a short spin
+  const uint64_t t_want = t_total + (d.fault ? 1u : 0u);
+  const uint32_t spin = d.fault ? 64u : d.spin_limit;
+  int t_lost = 0;                                  // (uniform) this block gave up waiting for T
   const bool ablock = int(blockIdx.x) < d.GA;
   const int b = ablock ? int(blockIdx.x) : int(blockIdx.x) - d.GA;
   const int ka0 = ablock ? int(int64_t(b) * d.nst / d.GA) : 0;        // K units of an A block
@@ -260,13 +278,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   // activation row 16 mt + lane % 16.  A partial stores acc in that order.
   auto frag_off = [&](int rg, int mt) __attribute__((always_inline)) { return uint32_t(((wave * 2 + rg) * MT + mt) * 1024 + lane * 16); };
 
-  auto store_partial = [&](float* P, uint32_t pbytes, uint32_t slot) __attribute__((always_inline)) {
+  // poison: NaN in place of the sums (this block's expand never got T)
+  auto store_partial = [&](float* P, uint32_t pbytes, uint32_t slot, bool poison) __attribute__((always_inline)) {
     const auto pres = make_rsrc(P, pbytes);
+    const f32x4 nan4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
 #pragma unroll
     for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt)
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc[rg][mt]), pres,
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, poison ? nan4 : acc[rg][mt]), pres,
                                                slot * uint32_t(G::FRAG) + frag_off(rg, mt), 0, kDeviceScope);
   };
 
@@ -305,18 +325,32 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     const int64_t fw = int64_t(key) * d.nst;
     const int64_t bw0 = pblock(fw, UW, d.GW);
     const int nWp = int(pblock(fw + d.nst - 1, UW, d.GW) - bw0 + 1);
-    store_partial(d.PW, d.pw_bytes, uint32_t(key * d.smaxW + (b - bw0)));
+    store_partial(d.PW, d.pw_bytes, uint32_t(key * d.smaxW + (b - bw0)), t_lost != 0);
     wait_vm<0>();          // the partial is out (device scope) before the count
     __syncthreads();
-    if (tid == 0) verdict = int(arrive(cW + key) + 1 == uint32_t(nWp));
+    // 1: this block is the tile's last; 2: the count was already past the tile's
+    // total (a counter area left non-zero), so this block stores NaN over the tile
+    if (tid == 0) {
+      const uint32_t old = arrive(cW + key, d.err, uint32_t(nWp));
+      verdict = old + 1 == uint32_t(nWp) ? 1 : old + 1 > uint32_t(nWp) ? 2 : 0;
+    }
     __syncthreads();
     if (verdict) {
+      const int v = verdict;
       f32x4 s[2][MT];
 #pragma unroll
       for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) s[rg][mt] = f32x4{};
-      sum_slots(s, d.PW, d.pw_bytes, uint32_t(key * d.smaxW), nWp);
+      if (v == 1) {
+        sum_slots(s, d.PW, d.pw_bytes, uint32_t(key * d.smaxW), nWp);
+      } else {
+        const f32x4 nan4{__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""), __builtin_nanf("")};
+#pragma unroll
+        for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) s[rg][mt] = nan4;
+      }
       const auto yres = make_rsrc(d.Y, d.y_bytes);
       const bool vec = (d.N & 3) == 0;
 #pragma unroll
@@ -349,9 +383,9 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
             }
           }
         }
-      if (tid == 0) {
+      if (tid == 0 && v == 1) {
         clear(cW + key);
-        if (arrive(cF) + 1 == uint32_t(d.ntW)) {   // the call is done: T and the A count are no longer read
+        if (arrive(cF, d.err, uint32_t(d.ntW)) + 1 == uint32_t(d.ntW)) {   // the call is done: T and the A count are no longer read
           clear(cA);
           clear(cT);
           clear(cF);
@@ -367,9 +401,13 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   // Expand units read T: the first of them is fetched only once every T piece
   // is stored.
   bool gated = false;
-  auto fetch_gate = [&]() __attribute__((always_inline)) {
+  // `word` is a word of the ring slot about to be refilled: every wave reads the
+  // verdict between the two barriers, before any load lands there.
+  auto fetch_gate = [&](int* word) __attribute__((always_inline)) {
     if (gated) return;
-    if (tid == 0) wait_for(cT, u64(nAt * MT * 2));
+    if (tid == 0) *word = wait_for(cT, t_want, spin, d.err) ? 0 : 1;
+    __syncthreads();
+    t_lost = *word;
     __syncthreads();
     gated = true;
   };
@@ -378,7 +416,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   // barrier.
   auto try_gate = [&](int* word) __attribute__((always_inline)) {
     if (gated) return true;
-    if (tid == 0) *word = __hip_atomic_load(cT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= u64(nAt * MT * 2);
+    if (tid == 0) *word = __hip_atomic_load(cT, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= t_want;
     __syncthreads();
     gated = *word != 0;
     __syncthreads();
@@ -404,7 +442,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
         if (p + 1 == n0) ci = c1;
         else advance(ci, K0);
       } else {
-        if (p == n0) fetch_gate();
+        if (p == n0) fetch_gate(reinterpret_cast<int*>(smem + (p % G::NS) * G::STAGE));
         issue(p % G::NS, ci, KIND_E);
         advance(ci, KIND_E);
       }
@@ -473,7 +511,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       if (i + 1 == n || (i + 1 < n0 && cc.key != key)) {
         __syncthreads();   // every wave is done with this stage's slot
         if constexpr (K0 == KIND_A) {
-          store_partial(d.PA, d.pa_bytes, uint32_t(key * d.GA + b));
+          store_partial(d.PA, d.pa_bytes, uint32_t(key * d.GA + b), false);
 #pragma unroll
           for (int rg = 0; rg < 2; ++rg)
 #pragma unroll
@@ -496,12 +534,17 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       run(std::integral_constant<Kind, KIND_A>{}, Cur{0, ka0, 0, 0, 0}, nAt * (ka1 - ka0), Cur{0, 0, 0, 0, 0}, 0);
     wait_vm<0>();
     __syncthreads();
-    if (tid == 0) arrive(cA);
+    // the ring is idle from here on: its first word carries this block's verdict
+    int* word = reinterpret_cast<int*>(smem);
+    if (tid == 0) *word = arrive(cA, d.err, uint32_t(d.GA)) + 1 > uint32_t(d.GA) ? 1 : 0;
     // A block with no T piece is done: it must not wait on the count either,
     // since the call's last tile clears it once every piece is in.
     if (b >= nAt * MT * 2) return;
-    if (tid == 0) wait_for(cA, u64(d.GA));   // every A block has stored its partials
+    // every A block has stored its partials; if that never happens (or the count
+    // was already past its total), this block's T pieces are stored as NaN
+    if (tid == 0 && !wait_for(cA, u64(d.GA), d.spin_limit, d.err)) *word = 1;
     __syncthreads();
+    const bool a_lost = *word != 0;
     // 2. T pieces (A tile g, 16-row tile mt, 16-column group rg), dealt round
     //    robin over the A blocks; each wave sums its own fragments of every A
     //    block's partial, all loads in flight at once.
@@ -528,7 +571,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
         float hi, lo;
-        split_hi_lo(mine ? at.scale[d.slot_adapter[sl]] * sum[e] : 0.0f, hi, lo);
+        split_hi_lo(a_lost ? __builtin_nanf("") : mine ? at.scale[d.slot_adapter[sl]] * sum[e] : 0.0f, hi, lo);
         hb[e] = bf16_bits(hi);
         lb[e] = bf16_bits(lo);
       }
@@ -540,7 +583,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
     }
     wait_vm<0>();           // T pieces are out before they are counted
     __syncthreads();
-    if (tid == 0 && done) arrive(cT, uint32_t(done));
+    if (tid == 0 && done) arrive(cT, d.err, t_total, uint32_t(done));
   } else {
     const int64_t uw0 = pstart(b, UW, d.GW), uw1 = pstart(b + 1, UW, d.GW);
     if (uw1 > uw0) {
@@ -629,6 +672,19 @@ DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t tr
   p.off_tl = p.off_th + r256(p.t_bytes);
   p.total = p.off_tl + r256(p.t_bytes);
   return p;
+}
+
+namespace {
+__global__ void clear_words_kernel(uint32_t* p, int n) {
+  for (int i = int(blockIdx.x * blockDim.x + threadIdx.x); i < n; i += int(gridDim.x * blockDim.x)) p[i] = 0;
+}
+}  // namespace
+
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  void* args[] = {&p, &n};
+  return hipLaunchKernel(reinterpret_cast<const void*>(&clear_words_kernel), dim3(unsigned((n + 255) / 256)),
+                         dim3(256), args, 0, stream);
 }
 
 hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,

@@ -78,11 +78,15 @@ constexpr int kDecodeMaxRows = 128;
 // every A_a tile each and then reduce T between them; W blocks split the W
 // units evenly, each followed by its share of the expand units (B_a against T)
 // of the tile its W units end in; the last block to finish a W tile sums the
-// tile's fp32 partials in block order.
+// tile's fp32 partials in block order.  A wait that gives up, or a count found
+// past its total, sets a sticky error bit in the last 8 bytes of the counter
+// area, and the outputs that depended on the lost hand-over are stored as NaN.
 constexpr int kDecodeTileRows = 128;
 constexpr int kDecodeUnitK = 64;
 constexpr int kDecodeBlocks = 256;      // one block per CU, all resident together
 constexpr int kDecodeMaxABlocks = 32;   // blocks that compute T = s X A^T
+constexpr uint32_t kDecodeErrTimeout = 1;   // a block gave up waiting for another block of its launch
+constexpr uint32_t kDecodeErrCount = 2;     // a hand-over count went past its total
 
 struct DecodeArgs {
   const void* X;
@@ -90,6 +94,7 @@ struct DecodeArgs {
   const void* WP;            // 4-bit params words [K/128][N], or null for bf16 weights
   void* Y;
   unsigned long long* cnt;   // counter area: arrivals per W tile, A blocks done, T pieces done, W tiles finished
+  uint32_t* err;             // sticky error bits (last 8 bytes of the counter area)
   float* PA;                 // [A tile][A block] partials, fragment-major
   float* PW;                 // [W tile][slot]
   uint16_t* TH;              // [n_used][M][trank] bf16 hi part of T
@@ -106,6 +111,8 @@ struct DecodeArgs {
   int32_t ntW;               // W tiles: ceil(N / 128)
   int32_t GA, GW;            // A blocks, W blocks
   int32_t smaxW;             // partial slots per W tile
+  uint32_t spin_limit;       // polls before a wait gives up
+  int32_t fault;             // test hook: waits for T target one piece more than exist
   int8_t row_slot[kDecodeMaxRows];           // slot of each row's adapter, -1 for base-only rows
   int8_t slot_adapter[LORA_MAX_ADAPTERS];    // adapter index of each slot
 };
@@ -119,6 +126,7 @@ struct DecodePlan {
   size_t off_cnt, off_pa, pa_bytes, off_pw, pw_bytes, off_th, t_bytes, off_tl, total;
 };
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t trank, int64_t n_used);
+int decode_mtiles(int64_t M);
 
 // Launchers (return the HIP status of the launch).
 hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at, const ShrinkPlan& sp,
@@ -128,6 +136,8 @@ hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const Adapter
                             hipEvent_t ev_start, hipEvent_t ev_stop);
 hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop);
+// Zero n 32-bit words on the stream (a kernel, so the fill may sit in a captured graph).
+hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream);
 // 4-bit weights: dequantize codes + params (N x K) into bf16 W (prefill path).
 hipError_t launch_q4_dequant(const void* codes, const void* params, void* w, int64_t N, int64_t K, hipStream_t stream);
 // Adapter extraction (lora_extract.hip).

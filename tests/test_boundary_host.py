@@ -54,7 +54,7 @@ def test_limits_match_header():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert bd.status_string(s)
     assert bd.status_string(99) == "unknown status"
 
@@ -66,13 +66,14 @@ def test_workspace_and_path_queries():
     assert bd.workspace_bytes(70, 17408, 5120, 256, dtype="f32") == C + 70 * 256 * 4
     assert bd.workspace_bytes(64, 512, 250, 16) == 0          # K not a multiple of 8
     assert bd.workspace_bytes(64, 512, 256, 24) == 0          # rank not a multiple of 16
-    # decode (<= 128 rows): split-K partials of W always, plus adapter partials
+    # decode (<= 128 rows): split-K partials of W always, plus adapter partials and T
     base = bd.workspace_bytes(70, 5120, 5120, 256, 0)
     one = bd.workspace_bytes(70, 5120, 5120, 256, 1)
     two = bd.workspace_bytes(70, 5120, 5120, 256, 2)
     assert 0 < base < one < two and base % 256 == 0 and base >= C + 70 * 5120 * 4
-    # decode counters (one per 128 output columns, plus three) must fit the counter area
-    n_fit = (C // 8 - 3) * 128
+    # decode counters (one per 128 output columns, plus three) must fit the counter area below the
+    # 8 bytes of error bits
+    n_fit = ((C - 8) // 8 - 3) * 128
     assert bd.path(70, n_fit, 8, 16) == "decode" and bd.workspace_bytes(70, n_fit, 8, 16) > 0
     assert bd.path(70, n_fit + 128, 8, 16) == "invalid" and bd.workspace_bytes(70, n_fit + 128, 8, 16) == 0
     assert bd.path(200, n_fit + 128, 8, 16) == "prefill"
