@@ -288,6 +288,43 @@ size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, 
  * ("invalid" for arguments lora_proj would reject).  A pure function of its arguments. */
 const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype);
 
+/*
+ * lora_proj_noalloc — lora_proj for callers that cannot allocate memory.
+ *
+ * For code under HIP graph capture, tight serving loops, or harnesses that forbid
+ * hipMalloc.  Arguments, checks and results are lora_proj's, without the
+ * workspace pair: the call's scratch (the decode path's counters, partial sums
+ * and T; the prefill path's T) lives in a fixed device array of
+ * LORA_NOALLOC_SCRATCH_BYTES inside the library, one copy per GPU, held from the
+ * first call on that GPU until the process ends.  The call allocates nothing (no
+ * hipMalloc, hipFree or allocating library routine); the caller still passes X,
+ * W, A, B and Y.
+ *
+ *   - A call whose scratch would exceed LORA_NOALLOC_SCRATCH_BYTES (see
+ *     lora_proj_workspace_bytes) returns LORA_EWORKSPACE and launches nothing.
+ *     At 64 MiB this covers every shape above at rank 256 up to 32,768 rows of
+ *     T (prefill) and every decode batch of up to 128 rows.
+ *   - Decode calls (at most 128 rows) first clear the array's counter area with
+ *     a small kernel on `stream`, so a call never depends on what an earlier one
+ *     left there.  A lost hand-over still gives NaN outputs (there is no status
+ *     query for the array).
+ *   - Every call on one GPU uses that GPU's one array: calls that overlap in
+ *     time on one GPU (different streams, threads or processes' contexts on the
+ *     same device) race and give wrong results.  Order them on one stream.
+ *   - The first call on a GPU looks up the array's device address (it must run
+ *     with that device current); a runtime failure there returns LORA_EHIP.
+ */
+#define LORA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+lora_status lora_proj_noalloc(const void* X,
+                              const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                              const void* W,
+                              const void* const* A, const void* const* B,
+                              int32_t n_adapters, int32_t rank, float scale,
+                              void* Y,
+                              int64_t M, int64_t N, int64_t K,
+                              lora_dtype dtype,
+                              hipStream_t stream);
+
 /* Static description of a status code; never NULL. */
 const char* lora_status_string(lora_status s);
 

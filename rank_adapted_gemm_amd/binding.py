@@ -26,7 +26,8 @@ EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "
            "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
            "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes",
            "lora_probe_mfma_bf16", "lora_probe_read", "lora_workspace_status", "lora_debug_handover_fault",
-           "lora_decode_plan_describe")
+           "lora_decode_plan_describe", "lora_proj_noalloc")
+NOALLOC_SCRATCH_BYTES = 64 << 20   # the device array lora_proj_noalloc uses instead of a workspace
 PLAN_FIELDS = ("MT", "nst", "nrs", "ntA", "ntW", "n_used", "GA", "GW", "smaxW", "off_cnt", "off_pa", "pa_bytes",
                "off_pw", "pw_bytes", "off_th", "t_bytes", "off_tl", "total")
 
@@ -85,6 +86,8 @@ def load():
     lib.lora_proj_path.restype = ctypes.c_char_p
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
+    lib.lora_proj_noalloc.argtypes = lib.lora_proj.argtypes[:15] + [vp]
+    lib.lora_proj_noalloc.restype = ctypes.c_int
     lib.lora_workspace_status.argtypes = [vp, sz, vp]
     lib.lora_workspace_status.restype = ctypes.c_int
     lib.lora_debug_handover_fault.argtypes = [i32]
@@ -380,3 +383,45 @@ def decode_plan(M: int, N: int, K: int, rank: int, n_used: int, slices=None) -> 
     if n == 0:
         return None
     return dict(zip(PLAN_FIELDS, list(out[:n])))
+
+
+def lora_proj_noalloc_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, dtype, stream=None) -> int:
+    """lora_proj_noalloc with raw device addresses (ints): lora_proj_raw without the workspace.
+    Returns the status code."""
+    lib = load()
+    starts = (ctypes.c_int32 * len(seg_starts))(*[int(v) for v in seg_starts])
+    adapt = (ctypes.c_int32 * max(len(seg_adapter), 1))(*[int(v) for v in seg_adapter])
+    n_ad = len(A)
+    a_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(a) if a else None for a in A])
+    b_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(b) if b else None for b in B])
+    return int(lib.lora_proj_noalloc(X, starts, adapt, len(seg_adapter), W, a_arr, b_arr, n_ad, int(rank),
+                                     float(scale), Y, int(M), int(N), int(K),
+                                     DTYPES[dtype] if isinstance(dtype, str) else int(dtype), stream))
+
+
+def lora_proj_noalloc(X, seg_starts, seg_adapter, W, A, B, scale, out, dtype=None, stream=None):
+    """lora_proj through the entry point that allocates nothing: the caller passes `out` (M, N) as
+    well as the inputs, and the library's fixed device array serves as the workspace."""
+    import torch
+    if dtype is None:
+        dtype = "f32" if X.dtype == torch.float32 else "bf16"
+    in_t = torch.float32 if dtype == "f32" else torch.bfloat16
+    out_t = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for t in (X, W, *A, *B):
+        if t.dtype != in_t or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"inputs must be contiguous {in_t} CUDA tensors")
+    M, K = X.shape
+    N = W.shape[0]
+    rank = A[0].shape[0] if len(A) else 0
+    if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
+    _check_operands(X.device, {"W": W, "out": out, **{f"A[{i}]": a for i, a in enumerate(A)},
+                               **{f"B[{i}]": b for i, b in enumerate(B)}},
+                    [("W", W, (N, K))] + [(f"A[{i}]", a, (rank, K)) for i, a in enumerate(A)]
+                    + [(f"B[{i}]", b, (N, rank)) for i, b in enumerate(B)])
+    s = _stream_of(stream, X.device)
+    st = lora_proj_noalloc_raw(X.data_ptr(), seg_starts, seg_adapter, W.data_ptr(), [a.data_ptr() for a in A],
+                               [b.data_ptr() for b in B], rank, scale, out.data_ptr(), M, N, K, dtype, s.cuda_stream)
+    if st != LORA_OK:
+        raise LoraError(st, status_string(st))
+    return out

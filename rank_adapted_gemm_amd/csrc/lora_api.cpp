@@ -11,6 +11,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <mutex>
 
 #include "lora_extract.h"
 #include "lora_internal.h"
@@ -200,7 +201,8 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
                      const void* W, const void* const* A, const void* const* B, int32_t n_adapters, int32_t rank,
                      const float* scales, float scale, int32_t n_slices, const int64_t* slice_n, void* Y,
                      int64_t M, int64_t N, int64_t K, lora_dtype dtype, void* workspace, size_t workspace_bytes,
-                     hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop, const void* WP = nullptr) {
+                     hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop, const void* WP = nullptr,
+                     bool clear_counters = false) {
   lora_status st = check_shape(M, N, K, dtype);
   if (st != LORA_OK) return st;
   const bool q4 = WP != nullptr;
@@ -365,7 +367,10 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
       for (int32_t m = tbl.start[g]; m < tbl.start[g + 1]; ++m)
         d.row_slot[m] = tbl.adapter[g] < 0 ? int8_t(-1) : slot_of[tbl.adapter[g]];
     for (int i = 0; i < n_used; ++i) d.slot_adapter[i] = slot_adapter[i];
-    e = lora::launch_decode(d, at, pl.MT, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
+    if (clear_counters)   // every check has passed: from here on the call launches
+      e = lora::launch_clear_words(reinterpret_cast<uint32_t*>(ws), int(LORA_WORKSPACE_COUNTER_BYTES / 4), stream);
+    if (e == hipSuccess)
+      e = lora::launch_decode(d, at, pl.MT, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
   } else if (dtype == LORA_F32) {
     if (has_adapter) e = lora::launch_f32_shrink(p, tbl, at, stream);
     if (e == hipSuccess) e = lora::launch_f32_main(p, tbl, at, has_adapter, stream, main_start, main_stop);
@@ -553,6 +558,57 @@ int32_t lora_decode_plan_describe(int64_t M, int64_t N, int64_t K, int32_t rank,
   const int32_t n = int32_t(sizeof(v) / sizeof(v[0]));
   for (int32_t i = 0; i < n && i < n_out; ++i) out[i] = v[i];
   return n;
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------ no allocation
+// The entry point for callers that cannot allocate (code under graph capture,
+// tight serving loops): its workspace is a fixed array in device memory, one
+// copy per GPU, held from the library's load until the process ends.  In host
+// code `scratch` names a host-side stand-in, never the device copy: the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current.
+static __device__ __align__(256) char scratch[LORA_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (null on a runtime error).
+void* scratch_of_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    g_scratch[dev] = p;
+  }
+  return g_scratch[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+lora_status lora_proj_noalloc(const void* X,
+                              const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                              const void* W,
+                              const void* const* A, const void* const* B,
+                              int32_t n_adapters, int32_t rank, float scale,
+                              void* Y,
+                              int64_t M, int64_t N, int64_t K,
+                              lora_dtype dtype,
+                              hipStream_t stream) {
+  void* ws = scratch_of_current_device();
+  if (!ws) return LORA_EHIP;
+  // the decode path's counters start from zero on every call: a failed earlier
+  // call on this GPU cannot leave counts behind for this one
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, nullptr, scale, 1, nullptr, Y, M, N,
+                  K, dtype, ws, LORA_NOALLOC_SCRATCH_BYTES, stream, nullptr, nullptr, nullptr, true);
 }
 
 }  // extern "C"
