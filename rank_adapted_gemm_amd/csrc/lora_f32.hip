@@ -6,20 +6,14 @@
 // a 4x4 register block each, 16-wide K slabs staged transposed in LDS, fused
 // multiply-adds in ascending k order.  Meant for tight parity checks of the
 // scheduling and indexing, not for speed.
-#include "lora_internal.h"
+#include "lora_device.h"
 
 namespace lora {
 namespace {
 
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-
 constexpr int T64 = 64;     // tile edge
 constexpr int FK = 16;      // K slab
 constexpr int PAD = 4;
-
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint32_t bytes) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
-}
 
 struct FSide {            // rows of a row-major fp32 matrix; rows outside [lo, hi) read as zero
   __amdgpu_buffer_rsrc_t res;
@@ -62,15 +56,6 @@ __device__ __forceinline__ void accumulate(float (&acc)[4][4], const FSide& ws, 
     }
     __syncthreads();
   }
-}
-
-__device__ __forceinline__ int first_segment(const SegTable& st, int m) {
-  int lo = 0, hi = st.n - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (st.start[mid] <= m) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 // Grid: (rank tiles) x (row tiles).  T[m, j] = s sum_k X[m, k] A_a[j, k] on adapter rows.
