@@ -104,14 +104,16 @@ typedef enum lora_dtype {
  *   workspace    device scratch of at least lora_proj_workspace_bytes(M, N, K, rank,
  *                n_adapters, dtype) bytes (may be NULL with size 0 when that is 0).  Its
  *                first LORA_WORKSPACE_COUNTER_BYTES are a counter area that the blocks of
- *                one decode launch (at most 128 rows) use to hand work to each other.  Every
- *                counter carries the number of the call that last counted on it, so counts
- *                left by earlier calls, finished or aborted, are ignored and the area never
- *                needs clearing between calls.  Its last 8 bytes hold sticky error bits
- *                (see lora_workspace_status), which must be zero when the workspace is
- *                first used: allocate it zero-filled.  The rest is scratch whose contents
- *                are not preserved.  Calls that share a workspace must not overlap in time
- *                (order them on one stream)
+ *                one decode launch (at most 128 rows) use to hand work to each other.  The
+ *                area must be zero when the workspace is first used (allocate it
+ *                zero-filled); every call that counts on a counter puts it back to zero, so
+ *                it needs no clearing between calls.  Counts left behind by a call that
+ *                never finished make later calls on the workspace wrong: where an arrival
+ *                finds a count past its total, the kernel stores NaN over the outputs it
+ *                owns and sets a sticky error bit in the area's last 8 bytes, which
+ *                lora_workspace_status reports before it restores the whole area.
+ *                The rest is scratch whose contents are not preserved.  Calls that share
+ *                a workspace must not overlap in time (order them on one stream)
  *   stream       HIP stream the work is ordered on (0 = the null stream)
  */
 lora_status lora_proj(const void* X,
