@@ -167,10 +167,8 @@ lora_status lora_proj_ex(const void* X,
  *   scales       HOST array of n_adapters floats (may be released on return);
  *                NULL with n_adapters > 0 returns LORA_EINVAL
  *
- * in place of the single `scale`.  All adapters of one call share `rank`.  An
- * adapter of smaller rank r_a is passed zero-padded to `rank` (A_a rows and B_a
- * columns r_a .. rank-1 zero): the padded terms add exact zeros, so the result
- * equals the one at rank r_a to the last bit.
+ * in place of the single `scale`.  All adapters of one call share `rank`;
+ * lora_proj_ranked takes adapters of different ranks, each stored compact.
  */
 lora_status lora_proj_multi(const void* X,
                             const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
@@ -220,6 +218,38 @@ lora_status lora_proj_sliced(const void* X,
                              const void* W,
                              const void* const* A, const void* const* B,
                              int32_t n_adapters, int32_t rank, const float* scales,
+                             int32_t n_slices, const int64_t* slice_n,
+                             void* Y,
+                             int64_t M, int64_t N, int64_t K,
+                             lora_dtype dtype,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream);
+
+/*
+ * lora_proj_ranked — lora_proj_sliced with each adapter at its own rank.
+ *
+ * Adapter a has rank ranks[a] (each 16 .. 512 and a multiple of 16, else
+ * LORA_EUNSUPPORTED): A[a] is (n_slices x ranks[a]) x K, slice s taking rows
+ * s ranks[a] .. (s + 1) ranks[a] - 1, and B[a] is N x ranks[a], both stored
+ * compact.  Each row gets its own adapter's term at that adapter's rank: an
+ * adapter of rank 64 beside one of rank 256 reads and multiplies 64-wide
+ * factors, not zero-padded 256-wide ones ("two 27B models on a single RTX 5090",
+ * section 4: every request is served with its own adapter).  The result equals
+ * lora_proj_sliced with every adapter zero-padded to the largest rank.
+ *
+ *   ranks        HOST, n_adapters int32 (entries of adapters no row names are ignored)
+ *   scales       HOST, n_adapters floats
+ *   workspace    at least lora_proj_sliced_workspace_bytes(M, N, K, r_max, n_slices,
+ *                n_adapters, dtype), r_max the largest rank of an adapter a row names
+ *
+ * Everything else, including the checks and errors, is lora_proj_sliced's;
+ * ranks or scales NULL with n_adapters > 0 is LORA_EINVAL.
+ */
+lora_status lora_proj_ranked(const void* X,
+                             const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                             const void* W,
+                             const void* const* A, const void* const* B,
+                             int32_t n_adapters, const int32_t* ranks, const float* scales,
                              int32_t n_slices, const int64_t* slice_n,
                              void* Y,
                              int64_t M, int64_t N, int64_t K,

@@ -26,7 +26,7 @@ EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "
            "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
            "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes",
            "lora_probe_mfma_bf16", "lora_probe_read", "lora_workspace_status", "lora_debug_handover_fault",
-           "lora_decode_plan_describe", "lora_proj_noalloc")
+           "lora_decode_plan_describe", "lora_proj_noalloc", "lora_proj_ranked")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # the device array lora_proj_noalloc uses instead of a workspace
 PLAN_FIELDS = ("MT", "nst", "nrs", "ntA", "ntW", "n_used", "GA", "GW", "smaxW", "off_cnt", "off_pa", "pa_bytes",
                "off_pw", "pw_bytes", "off_th", "t_bytes", "off_tl", "total")
@@ -66,6 +66,8 @@ def load():
     lib.lora_proj_sliced.argtypes = (lib.lora_proj_multi.argtypes[:10] + [i32, ctypes.POINTER(i64)] +
                                      lib.lora_proj_multi.argtypes[10:])
     lib.lora_proj_sliced.restype = ctypes.c_int
+    lib.lora_proj_ranked.argtypes = (lib.lora_proj_sliced.argtypes[:8] + [i32p] + lib.lora_proj_sliced.argtypes[9:])
+    lib.lora_proj_ranked.restype = ctypes.c_int
     lib.lora_proj_sliced_workspace_bytes.argtypes = [i64, i64, i64, i32, i32, i32, ctypes.c_int]
     lib.lora_proj_sliced_workspace_bytes.restype = sz
     lib.lora_proj_q4.argtypes = lib.lora_proj_sliced.argtypes[:5] + [vp] + lib.lora_proj_sliced.argtypes[5:]
@@ -342,6 +344,72 @@ def lora_proj(X, seg_starts, seg_adapter, W, A, B, scale, out=None, workspace=No
     st = lora_proj_raw(X.data_ptr(), seg_starts, seg_adapter, W.data_ptr(),
                        [a.data_ptr() for a in A], [b.data_ptr() for b in B], rank, scale,
                        out.data_ptr(), M, N, K, dtype, ws_ptr, ws_bytes, s.cuda_stream, events, slices)
+    if st != LORA_OK:
+        raise LoraError(st, status_string(st))
+    return out
+
+
+def lora_proj_ranked_raw(X, seg_starts, seg_adapter, W, A, B, ranks, scales, Y, M, N, K, dtype, workspace=None,
+                         workspace_bytes_=0, stream=None, slices=None) -> int:
+    """lora_proj_ranked with raw device addresses (ints): one rank and one scale per adapter.
+    Returns the status code."""
+    lib = load()
+    starts = (ctypes.c_int32 * len(seg_starts))(*[int(v) for v in seg_starts])
+    adapt = (ctypes.c_int32 * max(len(seg_adapter), 1))(*[int(v) for v in seg_adapter])
+    n_ad = len(A)
+    if len(ranks) != n_ad or len(scales) != n_ad:
+        raise ValueError("one rank and one scale per adapter")
+    a_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(a) if a else None for a in A])
+    b_arr = (ctypes.c_void_p * max(n_ad, 1))(*[ctypes.c_void_p(b) if b else None for b in B])
+    r_arg = (ctypes.c_int32 * max(n_ad, 1))(*[int(v) for v in ranks])
+    s_arg = (ctypes.c_float * max(n_ad, 1))(*[float(v) for v in scales])
+    widths = list(slices) if slices is not None else [int(N)]
+    w_arg = (ctypes.c_int64 * len(widths))(*[int(v) for v in widths])
+    return int(lib.lora_proj_ranked(X, starts, adapt, len(seg_adapter), W, a_arr, b_arr, n_ad, r_arg, s_arg,
+                                    len(widths), w_arg, Y, int(M), int(N), int(K),
+                                    DTYPES[dtype] if isinstance(dtype, str) else int(dtype), workspace,
+                                    int(workspace_bytes_), stream))
+
+
+def lora_proj_ranked(X, seg_starts, seg_adapter, W, A, B, scales, out=None, workspace=None, dtype=None, stream=None,
+                     slices=None):
+    """lora_proj with each adapter at its own rank r_a, read from its factors: A[a] is
+    (len(slices) * r_a, K) (slice s's factor in rows s r_a .. s r_a + r_a - 1), B[a] is (N, r_a).
+    ``scales``: one float per adapter.  Returns Y (M, N); raises LoraError on a non-OK status."""
+    import torch
+    if dtype is None:
+        dtype = "f32" if X.dtype == torch.float32 else "bf16"
+    in_t = torch.float32 if dtype == "f32" else torch.bfloat16
+    out_t = torch.bfloat16 if dtype == "bf16" else torch.float32
+    for t in [X, W, *A, *B]:
+        if t.dtype != in_t or not t.is_cuda or not t.is_contiguous():
+            raise ValueError(f"inputs must be contiguous {in_t} CUDA tensors")
+    M, K = X.shape
+    N = W.shape[0]
+    n_slices = 1 if slices is None else len(slices)
+    ranks = [int(a.shape[0]) // n_slices for a in A]
+    s = _stream_of(stream, X.device)
+    if out is None:
+        with torch.cuda.stream(s):
+            out = torch.empty((M, N), dtype=out_t, device=X.device)
+    if out.dtype != out_t or not out.is_contiguous() or tuple(out.shape) != (M, N):
+        raise ValueError("out must be a contiguous (M, N) tensor of the output dtype")
+    _check_operands(X.device, {"W": W, "out": out, "workspace": workspace,
+                               **{f"A[{i}]": a for i, a in enumerate(A)}, **{f"B[{i}]": b for i, b in enumerate(B)}},
+                    [("W", W, (N, K))]
+                    + [(f"A[{i}]", a, (n_slices * r, K)) for i, (a, r) in enumerate(zip(A, ranks))]
+                    + [(f"B[{i}]", b, (N, r)) for i, (b, r) in enumerate(zip(B, ranks))])
+    used = {int(a) for a in seg_adapter if int(a) >= 0}
+    rmax = max([ranks[a] for a in used], default=16)
+    need = workspace_bytes(M, N, K, rmax, len(A), dtype, n_slices)
+    if workspace is None and need:
+        with torch.cuda.stream(s):   # zero-filled on the call's stream: the counter area starts at zero
+            workspace = torch.zeros(need, dtype=torch.uint8, device=X.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else None
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    st = lora_proj_ranked_raw(X.data_ptr(), seg_starts, seg_adapter, W.data_ptr(), [a.data_ptr() for a in A],
+                              [b.data_ptr() for b in B], ranks, scales, out.data_ptr(), M, N, K, dtype, ws_ptr,
+                              ws_bytes, s.cuda_stream, slices)
     if st != LORA_OK:
         raise LoraError(st, status_string(st))
     return out

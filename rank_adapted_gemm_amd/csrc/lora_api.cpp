@@ -202,7 +202,7 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
                      const float* scales, float scale, int32_t n_slices, const int64_t* slice_n, void* Y,
                      int64_t M, int64_t N, int64_t K, lora_dtype dtype, void* workspace, size_t workspace_bytes,
                      hipStream_t stream, hipEvent_t main_start, hipEvent_t main_stop, const void* WP = nullptr,
-                     bool clear_counters = false) {
+                     bool clear_counters = false, const int32_t* ranks = nullptr) {
   lora_status st = check_shape(M, N, K, dtype);
   if (st != LORA_OK) return st;
   const bool q4 = WP != nullptr;
@@ -246,24 +246,31 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     tbl.start[tbl.n] = hi;
   }
 
-  // ---- adapters named by non-empty segments
+  // ---- adapters named by non-empty segments, each at its own rank (ranks
+  // NULL: every adapter at `rank`); from here on `rank` is the largest of them
   const bool has_adapter = adapter_rows > 0;
   const size_t ie = in_elem_bytes(dtype), oe = out_elem_bytes(dtype);
   AdapterTable at;
   memset(&at, 0, sizeof(at));
-  const size_t a_bytes = size_t(rank > 0 ? rank : 0) * size_t(sl.n) * size_t(K) * ie;
-  const size_t b_bytes = size_t(N) * size_t(rank > 0 ? rank : 0) * ie;
   if (has_adapter) {
-    if (!rank_ok(rank)) return LORA_EUNSUPPORTED;
-    if (int64_t(a_bytes) >= kMaxOperandBytes || int64_t(b_bytes) >= kMaxOperandBytes) return LORA_EUNSUPPORTED;
+    int32_t rmax = 0;
     for (int a = 0; a < n_adapters; ++a) {
       if (!used[a]) continue;
+      const int32_t ra = ranks ? ranks[a] : rank;
+      if (!rank_ok(ra)) return LORA_EUNSUPPORTED;
+      const size_t ab = size_t(ra) * size_t(sl.n) * size_t(K) * ie, bb = size_t(N) * size_t(ra) * ie;
+      if (int64_t(ab) >= kMaxOperandBytes || int64_t(bb) >= kMaxOperandBytes) return LORA_EUNSUPPORTED;
       if (!A[a] || !B[a]) return LORA_EADAPTER;
       if (!aligned16(A[a]) || !aligned16(B[a])) return LORA_EINVAL;
       at.A[a] = A[a];
       at.B[a] = B[a];
       at.scale[a] = scales ? scales[a] : scale;
+      at.rank[a] = ra;
+      at.a_bytes[a] = uint32_t(ab);
+      at.b_bytes[a] = uint32_t(bb);
+      rmax = ra > rmax ? ra : rmax;
     }
+    rank = rmax;
   }
 
   // ---- workspace
@@ -298,9 +305,9 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
   if (has_adapter) {
     for (int a = 0; a < n_adapters; ++a) {
       if (!used[a]) continue;
-      if (overlaps(Y, y_bytes, A[a], a_bytes) || overlaps(Y, y_bytes, B[a], b_bytes)) return LORA_EINVAL;
-      if (overlaps(workspace, need, A[a], a_bytes) || overlaps(workspace, need, B[a], b_bytes))
-        return LORA_EINVAL;
+      const size_t ab = at.a_bytes[a], bb = at.b_bytes[a];
+      if (overlaps(Y, y_bytes, A[a], ab) || overlaps(Y, y_bytes, B[a], bb)) return LORA_EINVAL;
+      if (overlaps(workspace, need, A[a], ab) || overlaps(workspace, need, B[a], bb)) return LORA_EINVAL;
     }
   }
 
@@ -319,8 +326,6 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
   p.w_bytes = uint32_t(w_bytes);
   p.y_bytes = uint32_t(y_bytes);
   p.t_bytes = has_adapter && !decode ? uint32_t(t_bytes(M, int64_t(rank) * sl.n)) : 0u;
-  p.a_bytes = uint32_t(a_bytes);
-  p.b_bytes = uint32_t(b_bytes);
 
   hipError_t e = hipSuccess;
   if (decode) {
@@ -342,10 +347,13 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     d.x_bytes = uint32_t(x_bytes);
     d.w_bytes = uint32_t(w_bytes);
     d.y_bytes = uint32_t(y_bytes);
-    d.a_bytes = uint32_t(a_bytes);
-    d.b_bytes = uint32_t(b_bytes);
     d.t_bytes = uint32_t(pl.t_bytes);
     d.pa_bytes = uint32_t(pl.pa_bytes);
+    d.ranks_differ = 0;
+    for (int a = 0; a < n_adapters; ++a)
+      if (used[a] && at.rank[a] != rank) d.ranks_differ = 1;
+    d.a_bytes = has_adapter ? uint32_t(size_t(rank) * size_t(sl.n) * size_t(K) * ie) : 0u;
+    d.b_bytes = has_adapter ? uint32_t(size_t(N) * size_t(rank) * ie) : 0u;
     d.pw_bytes = uint32_t(pl.pw_bytes);
     d.M = int32_t(M);
     d.N = int32_t(N);
@@ -468,6 +476,23 @@ lora_status lora_proj_sliced(const void* X,
   if (n_adapters > 0 && !scales) return LORA_EINVAL;
   return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, rank, scales, 0.0f, n_slices, slice_n, Y,
                   M, N, K, dtype, workspace, workspace_bytes, stream, nullptr, nullptr);
+}
+
+lora_status lora_proj_ranked(const void* X,
+                             const int32_t* seg_starts, const int32_t* seg_adapter, int32_t n_seg,
+                             const void* W,
+                             const void* const* A, const void* const* B,
+                             int32_t n_adapters, const int32_t* ranks, const float* scales,
+                             int32_t n_slices, const int64_t* slice_n,
+                             void* Y,
+                             int64_t M, int64_t N, int64_t K,
+                             lora_dtype dtype,
+                             void* workspace, size_t workspace_bytes,
+                             hipStream_t stream) {
+  if (n_adapters > 0 && (!scales || !ranks)) return LORA_EINVAL;
+  return run_call(X, seg_starts, seg_adapter, n_seg, W, A, B, n_adapters, LORA_MIN_RANK, scales, 0.0f, n_slices,
+                  slice_n, Y, M, N, K, dtype, workspace, workspace_bytes, stream, nullptr, nullptr, nullptr, false,
+                  ranks);
 }
 
 }  // extern "C"

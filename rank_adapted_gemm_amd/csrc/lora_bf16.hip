@@ -353,6 +353,8 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
   while (a + 1 < sp.n_adapters && sp.tile_off[a + 1] <= tv) ++a;
   const int v0 = (tv - sp.tile_off[a]) * C::TM, nrows = min(C::TM, sp.rows[a] - v0);
   const int j0 = tn * C::TN;
+  const int atrank = p.sl.n * at.rank[a];      // rows of A_a
+  if (j0 >= atrank) return;                    // a rank tile past this adapter's rank (whole block)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wn = wave % C::WN, wm = wave / C::WN;
   const auto tres = make_rsrc(p.T, p.t_bytes);
@@ -378,7 +380,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
   }
   __syncthreads();
 
-  const Side as{make_rsrc_words(at.A[a], p.a_bytes), uint32_t(p.K) * 2u, j0, 0, p.trank};
+  const Side as{make_rsrc_words(at.A[a], at.a_bytes[a]), uint32_t(p.K) * 2u, j0, 0, atrank};
   const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, 0, 0, 0};
   f32x16 acc[C::FN][C::FM];
 #pragma unroll
@@ -454,11 +456,10 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
   // name another adapter or none masked to zero: one pass per adapter however
   // many segments it has in the tile (each row's own adapter adds its term in
   // one pass, the other passes add exact zeros).  The tile's slice reads its
-  // own r columns of T (a tile never straddles two slices).
+  // own r_a columns of T (a tile never straddles two slices).
   if (has_adapter) {
-    const uint32_t tcol = uint32_t(slice_of(p.sl, n0) * p.rank) * 2u;
-    const i32x4 tres = make_rsrc_words(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
-    const uint32_t ld = uint32_t(p.rank) * 2u, tld = uint32_t(p.trank) * 2u;
+    const int slice = slice_of(p.sl, n0);
+    const uint32_t tld = uint32_t(p.trank) * 2u;
     const int lo_row0 = m0 + p.M;          // T_lo rows sit M rows after T_hi rows
     uint32_t seen = 0;                     // adapters already applied to this tile
     for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
@@ -469,12 +470,17 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
 #pragma unroll
       for (int j = 0; j < C::FM; ++j)
         keep |= row_adapter[wm * (C::TM / C::WM) + j * 32 + (lane & 31)] == a ? 1u << j : 0u;
-      const Side bs{make_rsrc_words(at.B[a], p.b_bytes), ld, n0, 0, p.N};
+      // adapter a's rank: B_a's row stride, the tile's slice of T (r_a columns
+      // from slice x r_a), and the number of stages
+      const int ra = at.rank[a];
+      const uint32_t ld = uint32_t(ra) * 2u, tcol = uint32_t(slice * ra) * 2u;
+      const i32x4 tres = make_rsrc_words(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
+      const Side bs{make_rsrc_words(at.B[a], at.b_bytes[a]), ld, n0, 0, p.N};
       const Side th{tres, tld, m0, 0, 0};
       const Side tl{tres, tld, lo_row0, 0, 0};
-      const int nr = 2 * ((p.rank + BK - 1) / BK);
+      const int nr = 2 * ((ra + BK - 1) / BK);
       auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
-      k_loop_pingpong<C, true>(acc, nr, p.rank, src, smem, tid, wn, wm, keep);
+      k_loop_pingpong<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
     }
   }
 

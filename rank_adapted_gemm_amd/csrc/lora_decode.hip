@@ -123,20 +123,31 @@ struct Unit {
   uint32_t wbase, wld, xbase, xld;
 };
 
+// RANKED: adapters of different ranks; each adapter's rank, row stride and
+// extents are looked up per unit, and expand units past an adapter's rank move
+// no data.  Otherwise every adapter has the call's rank (the common case keeps
+// its own instantiation, free of those lookups).
+template <bool RANKED>
 __device__ inline Unit unit_of(const Cur& c, Kind kind, const DecodeArgs& d, const AdapterTable& at) {
   Unit x;
-  if (kind == KIND_E) {   // B_a's rows of the tile against the tile's slice of T (r columns)
-    x.wres = make_rsrc_words(at.B[d.slot_adapter[c.slot]], d.b_bytes);
-    x.wld = uint32_t(d.rank) * 2u;
-    x.wbase = uint32_t(c.key * TR) * x.wld + uint32_t(c.st) * RB;
+  if (kind == KIND_E) {   // B_a's rows of the tile against the tile's slice of T (r_a columns)
+    const int a = d.slot_adapter[c.slot];
+    const int ra = RANKED ? at.rank[a] : d.rank;
+    x.wres = make_rsrc_words(at.B[a], RANKED ? at.b_bytes[a] : d.b_bytes);
+    x.wld = uint32_t(ra) * 2u;
     x.xres = make_rsrc_words(c.hl ? d.TL : d.TH, d.t_bytes);
     x.xld = uint32_t(d.trank) * 2u;
-    x.xbase = uint32_t(c.slot * d.M) * x.xld + uint32_t(slice_of(d.sl, c.key * TR) * d.rank) * 2u +
-              uint32_t(c.st) * RB;
+    x.wbase = uint32_t(c.key * TR) * x.wld + uint32_t(c.st) * RB;
+    x.xbase = uint32_t(c.slot * d.M) * x.xld + uint32_t(slice_of(d.sl, c.key * TR) * ra) * 2u + uint32_t(c.st) * RB;
+    if (RANKED && c.st * UK >= ra) {   // past this adapter's rank: no traffic (the multiply zeroes it too)
+      x.wbase = kMaskedOffset;
+      x.xbase = kMaskedOffset;
+    }
   } else {
     x.wld = uint32_t(d.K) * 2u;
     if (kind == KIND_A) {
-      x.wres = make_rsrc_words(at.A[d.slot_adapter[c.slot]], d.a_bytes);
+      const int a = d.slot_adapter[c.slot];
+      x.wres = make_rsrc_words(at.A[a], RANKED ? at.a_bytes[a] : d.a_bytes);
       x.wbase = uint32_t(c.at * TR) * x.wld + uint32_t(c.st) * RB;
     } else {
       x.wres = make_rsrc_words(d.W, d.w_bytes);
@@ -163,7 +174,7 @@ __device__ inline bool wait_for(u64* c, u64 want, uint32_t limit, uint32_t* err)
 // Q4: the base weights come as 4-bit codes plus per-group params (see
 // lora_proj_q4); W units then carry 4 KiB of codes and their params instead of
 // 16 KiB of bf16, and the multiply dequantizes the weight fragments to bf16.
-template <int MT, bool F32_OUT, bool Q4>
+template <int MT, bool F32_OUT, bool Q4, bool RANKED>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable at) {
   using G = DG<MT>;
   __shared__ __attribute__((aligned(1024))) char smem[G::NS * G::STAGE];
@@ -223,7 +234,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   const int xcount = XQ + (wave < XREM ? 1 : 0);
   const int xfirst = wave * XQ + min(wave, XREM);
   auto issue = [&](int slot, const Cur& c, Kind kind) __attribute__((always_inline)) {
-    const Unit x = unit_of(c, kind, d, at);
+    const Unit x = unit_of<RANKED>(c, kind, d, at);
     const uint32_t dst = lbase + uint32_t(slot) * G::STAGE;
     if (Q4 && kind == KIND_W) {
       // wave w's 4 KiB: codes of its 32 rows (32 bytes each, row-major), then
@@ -463,7 +474,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       }
       const char* ws = smem + (i % G::NS) * G::STAGE;
       const char* xs = ws + TR * RB;
-      const int lim = K == KIND_E ? d.rank : d.K, e0 = cc.st * UK;
+      const int lim = K == KIND_E ? (RANKED ? at.rank[d.slot_adapter[cc.slot]] : d.rank) : d.K, e0 = cc.st * UK;
       const bool tail = lim - e0 < UK;
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
@@ -621,13 +632,18 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
   }
 }
 
+// 4-bit calls take one rank for every adapter (lora_proj_q4), so only the bf16
+// kernels come in a RANKED form.
 template <int MT>
-const void* pick(bool f32_out, bool q4) {
+const void* pick(bool f32_out, bool q4, bool ranked) {
   if (q4)
-    return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, true>)
-                   : reinterpret_cast<const void*>(&decode_kernel<MT, false, true>);
-  return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, false>)
-                 : reinterpret_cast<const void*>(&decode_kernel<MT, false, false>);
+    return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, true, false>)
+                   : reinterpret_cast<const void*>(&decode_kernel<MT, false, true, false>);
+  if (ranked)
+    return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, false, true>)
+                   : reinterpret_cast<const void*>(&decode_kernel<MT, false, false, true>);
+  return f32_out ? reinterpret_cast<const void*>(&decode_kernel<MT, true, false, false>)
+                 : reinterpret_cast<const void*>(&decode_kernel<MT, false, false, false>);
 }
 
 }  // namespace
@@ -689,11 +705,12 @@ hipError_t launch_clear_words(uint32_t* p, int n, hipStream_t stream) {
 
 hipError_t launch_decode(const DecodeArgs& d, const AdapterTable& at, int MT, bool f32_out, hipStream_t stream,
                          hipEvent_t ev_start, hipEvent_t ev_stop) {
-  const bool q4 = d.WP != nullptr;
-  const void* k = MT == 2   ? pick<2>(f32_out, q4)
-                  : MT == 4 ? pick<4>(f32_out, q4)
-                  : MT == 5 ? pick<5>(f32_out, q4)
-                            : pick<8>(f32_out, q4);
+  const bool q4 = d.WP != nullptr, ranked = d.ranks_differ != 0;
+  if (q4 && ranked) return hipErrorInvalidValue;
+  const void* k = MT == 2   ? pick<2>(f32_out, q4, ranked)
+                  : MT == 4 ? pick<4>(f32_out, q4, ranked)
+                  : MT == 5 ? pick<5>(f32_out, q4, ranked)
+                            : pick<8>(f32_out, q4, ranked);
   DecodeArgs dd = d;
   AdapterTable aa = at;
   void* args[] = {&dd, &aa};

@@ -71,7 +71,7 @@ __global__ __launch_bounds__(256) void f32_shrink_kernel(ProjArgs p, SegTable st
     if (a < 0) continue;
     const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
     float acc[4][4] = {};
-    const FSide as{make_rsrc(at.A[a], p.a_bytes), uint32_t(p.K) * 4u, j0, 0, p.trank};
+    const FSide as{make_rsrc(at.A[a], at.a_bytes[a]), uint32_t(p.K) * 4u, j0, 0, p.sl.n * at.rank[a]};
     const FSide xs{xres, uint32_t(p.K) * 4u, m0, lo, hi};
     accumulate(acc, as, xs, p.K, xl, wl, tid);
 #pragma unroll
@@ -101,16 +101,17 @@ __global__ __launch_bounds__(256) void f32_main_kernel(ProjArgs p, SegTable st, 
     const FSide xs{make_rsrc(p.X, p.x_bytes), uint32_t(p.K) * 4u, m0, 0, p.M};
     accumulate(acc, ws, xs, p.K, xl, wl, tid);
   }
-  if (has_adapter) {   // the tile's slice reads its own r columns of T
-    const uint32_t tcol = uint32_t(slice_of(p.sl, n0) * p.rank) * 4u;
-    const auto tres = make_rsrc(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
+  if (has_adapter) {   // the tile's slice reads its own r_a columns of T
+    const int slice = slice_of(p.sl, n0);
     for (int g = first_segment(st, m0); g < st.n && st.start[g] < m1; ++g) {
       const int a = st.adapter[g];
       if (a < 0) continue;
-      const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1);
-      const FSide bs{make_rsrc(at.B[a], p.b_bytes), uint32_t(p.rank) * 4u, n0, 0, p.N};
+      const int lo = max(st.start[g], m0), hi = min(st.start[g + 1], m1), ra = at.rank[a];
+      const uint32_t tcol = uint32_t(slice * ra) * 4u;
+      const auto tres = make_rsrc(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
+      const FSide bs{make_rsrc(at.B[a], at.b_bytes[a]), uint32_t(ra) * 4u, n0, 0, p.N};
       const FSide ts{tres, uint32_t(p.trank) * 4u, m0, lo, hi};
-      accumulate(acc, bs, ts, p.rank, xl, wl, tid);
+      accumulate(acc, bs, ts, ra, xl, wl, tid);
     }
   }
   const auto yres = make_rsrc(p.Y, p.y_bytes);

@@ -31,10 +31,16 @@ struct ShrinkPlan {
   int32_t tile_off[LORA_MAX_ADAPTERS + 1];
 };
 
+// Adapter a has its own rank r_a (at most the call's rank r, the largest of
+// them): A_a is (S r_a) x K and B_a is N x r_a, and its rows of T hold S r_a
+// values (columns S r_a .. S r - 1 are never read for them).
 struct AdapterTable {
-  const void* A[LORA_MAX_ADAPTERS];           // (S r) x K each (device), S = number of slices
-  const void* B[LORA_MAX_ADAPTERS];           // N x r each (device)
+  const void* A[LORA_MAX_ADAPTERS];           // (S r_a) x K each (device), S = number of slices
+  const void* B[LORA_MAX_ADAPTERS];           // N x r_a each (device)
   float scale[LORA_MAX_ADAPTERS];             // s of each adapter's rows
+  int32_t rank[LORA_MAX_ADAPTERS];            // r_a (0 for adapters no row names)
+  uint32_t a_bytes[LORA_MAX_ADAPTERS];        // extent of A_a
+  uint32_t b_bytes[LORA_MAX_ADAPTERS];        // extent of B_a
 };
 
 // Shapes and buffers of one call.  Byte extents bound every buffer access:
@@ -59,11 +65,10 @@ struct ProjArgs {
   const void* W;
   void* Y;
   void* T;            // workspace: s_a X A_a^T for adapter rows, indexed by global row
-  int32_t M, N, K, rank;
-  int32_t trank;      // width of T and rows of every A_a: slices x rank
+  int32_t M, N, K, rank;   // rank: the largest adapter rank of the call
+  int32_t trank;      // width of T: slices x rank
   Slices sl;
   uint32_t x_bytes, w_bytes, y_bytes, t_bytes;
-  uint32_t a_bytes, b_bytes;   // extent of every A_a / B_a
 };
 
 // Byte offset used for masked accesses: past the end of every operand
@@ -99,10 +104,12 @@ struct DecodeArgs {
   float* PW;                 // [W tile][slot]
   uint16_t* TH;              // [n_used][M][trank] bf16 hi part of T
   uint16_t* TL;              // [n_used][M][trank] bf16 lo part of T
-  uint32_t x_bytes, w_bytes, y_bytes, a_bytes, b_bytes, t_bytes, pa_bytes, pw_bytes;
+  uint32_t x_bytes, w_bytes, y_bytes, t_bytes, pa_bytes, pw_bytes;
+  uint32_t a_bytes, b_bytes; // extent of every A_a / B_a when all used adapters have rank `rank`
+  int32_t ranks_differ;      // 1: adapters of different ranks (the kernel that reads each adapter's)
   uint32_t wp_bytes;
-  int32_t M, N, K, rank;
-  int32_t trank;             // width of T and rows of every A_a: slices x rank
+  int32_t M, N, K, rank;     // rank: the largest adapter rank of the call
+  int32_t trank;             // width of T: slices x rank
   Slices sl;
   int32_t nst;               // units per tile along K: ceil(K / 64)
   int32_t nrs;               // expand units per tile per half: ceil(rank / 64)

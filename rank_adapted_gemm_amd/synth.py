@@ -203,11 +203,15 @@ def workload_problem(name: str, layer: int = 0, proj: int = 0, x=None) -> Proble
 
 def random_problem(seed: int, M: int, N: int, K: int, rank: int, seg_starts, seg_adapter,
                    n_adapters: int = 1, scale=1.0, dtype: str = "bf16",
-                   sigma_x: float = 1.0, sigma_w: float = SIGMA_WAB, integer: bool = False) -> Problem:
+                   sigma_x: float = 1.0, sigma_w: float = SIGMA_WAB, integer: bool = False,
+                   ranks=None, slices: int = 1) -> Problem:
     """A seeded problem of any shape, for parity sweeps and edge cases.
 
     ``integer`` draws integers in {-2..2} instead of Gaussians (exact in every
-    precision the path uses).
+    precision the path uses).  ``ranks``: one rank per adapter (then ``rank`` is
+    ignored), with A[a] of (slices * ranks[a]) x K (the slices' factors stacked)
+    and B[a] of N x ranks[a]; by default every adapter has A of rank x K and B
+    of N x rank.
     """
     g = np.random.Generator(np.random.PCG64(seed))
 
@@ -218,11 +222,17 @@ def random_problem(seed: int, M: int, N: int, K: int, rank: int, seg_starts, seg
 
     X = draw((M, K), sigma_x)
     W = draw((N, K), sigma_w)
-    A = [draw((rank, K), sigma_w) for _ in range(n_adapters)]
-    B = [draw((N, rank), sigma_w) for _ in range(n_adapters)]
+    if ranks is None:
+        A = [draw((rank, K), sigma_w) for _ in range(n_adapters)]
+        B = [draw((N, rank), sigma_w) for _ in range(n_adapters)]
+    else:
+        if len(ranks) != n_adapters:
+            raise ValueError("one rank per adapter")
+        A = [draw((slices * r, K), sigma_w) for r in ranks]
+        B = [draw((N, r), sigma_w) for r in ranks]
     p = Problem(X=X, W=W, A=A, B=B, seg_starts=np.asarray(seg_starts, np.int32),
                 seg_adapter=np.asarray(seg_adapter, np.int32), scale=scale, dtype=dtype,
-                name=f"random(seed={seed},M={M},N={N},K={K},r={rank})")
+                name=f"random(seed={seed},M={M},N={N},K={K},r={rank if ranks is None else list(ranks)})")
     if dtype == "bf16":
         p.X_bits = f32_to_bf16_bits(X)
         p.W_bits = f32_to_bf16_bits(W)

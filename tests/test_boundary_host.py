@@ -193,6 +193,50 @@ def test_sliced_workspace_query():
     assert bd.workspace_bytes(70, 15000, 5120, 256, 1, "bf16", 3) == 0       # N not slice-aligned
 
 
+def ranked_call(**kw):
+    a = dict(X=FAKE, seg_starts=[0, 32, 48, 64], seg_adapter=[-1, 0, 1], W=FAKE2, A=[FAKE3, FAKE3 + (1 << 22)],
+             B=[FAKE4, FAKE4 + (1 << 22)], ranks=[16, 48], scales=[0.5, 1.0], Y=FAKE5, M=64, N=512, K=256,
+             dtype="bf16", workspace=FAKE * 320, workspace_bytes_=1 << 24, stream=None)
+    a.update(kw)
+    return bd.lora_proj_ranked_raw(**a)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(ranks=[16, 24]), bd.LORA_EUNSUPPORTED),               # a rank not a multiple of 16
+    (dict(ranks=[528, 16]), bd.LORA_EUNSUPPORTED),              # above the largest rank
+    (dict(ranks=[0, 48]), bd.LORA_EUNSUPPORTED),                # a named adapter with no rank
+    (dict(ranks=[16, 48], seg_adapter=[-1, 0, 2]), bd.LORA_EADAPTER),
+    (dict(A=[FAKE3, None]), bd.LORA_EADAPTER),
+    (dict(Y=FAKE3 + (1 << 22) + 4096), bd.LORA_EINVAL),          # Y overlaps the rank-48 adapter's A
+    # the workspace of the largest rank (48) is needed: one sized for rank 16 is too small
+    (dict(M=300, seg_starts=[0, 32, 48, 300], workspace_bytes_=bd.workspace_bytes(300, 512, 256, 16, 2)),
+     bd.LORA_EWORKSPACE),
+])
+def test_ranked_rejected_before_launch(kw, code):
+    assert ranked_call(**kw) == code
+
+
+def test_ranked_checks():
+    # an empty batch is a no-op whatever the ranks
+    assert ranked_call(ranks=[16, 7], seg_adapter=[-1, 0, 0], M=0, seg_starts=[0, 0, 0, 0], X=None,
+                       Y=None) == bd.LORA_OK
+    with pytest.raises(ValueError):
+        ranked_call(ranks=[16])                                  # one rank per adapter
+    lib = bd.load()
+    starts = (ctypes.c_int32 * 3)(0, 32, 64)
+    adapt = (ctypes.c_int32 * 2)(-1, 0)
+    a_arr = (ctypes.c_void_p * 1)(FAKE3)
+    b_arr = (ctypes.c_void_p * 1)(FAKE4)
+    widths = (ctypes.c_int64 * 1)(512)
+    scales = (ctypes.c_float * 1)(0.5)
+    ranks = (ctypes.c_int32 * 1)(16)
+    # NULL ranks or NULL scales with adapters present
+    for r, sc in ((None, scales), (ranks, None)):
+        st = lib.lora_proj_ranked(FAKE, starts, adapt, 2, FAKE2, a_arr, b_arr, 1, r, sc, 1, widths, FAKE5,
+                                  64, 512, 256, bd.DTYPES["bf16"], FAKE * 320, 1 << 24, None)
+        assert st == bd.LORA_EINVAL
+
+
 def q4_call(**kw):
     a = dict(X=FAKE, seg_starts=[0, 32, 64], seg_adapter=[-1, 0], Wq=FAKE2, Wp=FAKE2 + (1 << 19), A=[FAKE3],
              B=[FAKE4], rank=16, scales=[0.5], Y=FAKE5, M=64, N=512, K=256, dtype="bf16", workspace=FAKE * 320,
