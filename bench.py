@@ -380,6 +380,88 @@ def run_prefill_mixed(a, dev, hip):
                 adapter_rows=ma)
 
 
+RANKED_RANKS = (64, 128, 192, 256)
+
+
+def run_ranked(a, dev):
+    """Adapters of different ranks in one batch: four adapters of ranks 64, 128, 192 and 256 per
+    projection over one layer, served with compact factors (lora_proj_ranked) and, for comparison,
+    zero-padded to rank 256 (lora_proj_multi); prefill16k's 212-segment table and a 70-row decode
+    batch (4 x 16 adapter rows, 6 base rows).  ms per step of 7 calls, each variant timed alone."""
+    import torch
+    out = {}
+    for path, wname, M in (("prefill", "prefill16k", 16384), ("decode", "suffix", 70)):
+        cfg = synth.WORKLOADS[wname]["cfg"]
+        layer = device_layer(cfg, 0, M, dev)
+        if path == "prefill":
+            starts, labels = synth.mixed_table(M, len(RANKED_RANKS))
+        else:
+            starts, labels = [0, 16, 32, 48, 64, 70], [0, 1, 2, 3, -1]
+        rows = [0] * len(RANKED_RANKS)
+        for g, lab in enumerate(labels):
+            if lab >= 0:
+                rows[lab] += starts[g + 1] - starts[g]
+        flops = 0
+        for pi, p in enumerate(layer):
+            A, B, Ap, Bp = [], [], [], []
+            for j, r in enumerate(RANKED_RANKS):
+                aj = synth.device_normal_bf16((r, p["K"]), synth.SIGMA_WAB,
+                                              synth.extra_adapter_seed(cfg, 0, pi, synth.T_A, j + 1), dev)
+                bj = synth.device_normal_bf16((p["N"], r), synth.SIGMA_WAB,
+                                              synth.extra_adapter_seed(cfg, 0, pi, synth.T_B, j + 1), dev)
+                ap = torch.zeros((synth.RANK, p["K"]), dtype=torch.bfloat16, device=dev)
+                ap[:r] = aj
+                bp = torch.zeros((p["N"], synth.RANK), dtype=torch.bfloat16, device=dev)
+                bp[:, :r] = bj
+                A.append(aj), B.append(bj), Ap.append(ap), Bp.append(bp)
+                flops += 2 * rows[j] * r * (p["K"] + p["N"])
+            p["A"], p["B"], p["Ap"], p["Bp"] = A, B, Ap, Bp
+            flops += 2 * M * p["N"] * p["K"]
+        scales = [1.0] * len(RANKED_RANKS)
+        ws = torch.zeros(max(bd.workspace_bytes(M, p["N"], p["K"], synth.RANK, len(RANKED_RANKS)) for p in layer),
+                         dtype=torch.uint8, device=dev)
+        outs = {p["N"]: torch.empty((M, p["N"]), dtype=torch.bfloat16, device=dev) for p in layer}
+        stream = torch.cuda.current_stream(dev).cuda_stream
+
+        def step(padded):
+            for p in layer:
+                if padded:
+                    st = bd.lora_proj_raw(p["X"].data_ptr(), starts, labels, p["W"].data_ptr(),
+                                          [t.data_ptr() for t in p["Ap"]], [t.data_ptr() for t in p["Bp"]],
+                                          synth.RANK, scales, outs[p["N"]].data_ptr(), M, p["N"], p["K"], "bf16",
+                                          ws.data_ptr(), ws.numel(), stream)
+                else:
+                    st = bd.lora_proj_ranked_raw(p["X"].data_ptr(), starts, labels, p["W"].data_ptr(),
+                                                 [t.data_ptr() for t in p["A"]], [t.data_ptr() for t in p["B"]],
+                                                 RANKED_RANKS, scales, outs[p["N"]].data_ptr(), M, p["N"], p["K"],
+                                                 "bf16", ws.data_ptr(), ws.numel(), stream)
+                if st != bd.LORA_OK:
+                    raise bd.LoraError(st, bd.status_string(st))
+
+        res = {}
+        for padded in (False, True):
+            for _ in range(a.warmup):
+                step(padded)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(a.steps):
+                step(padded)
+            torch.cuda.synchronize()
+            res["padded" if padded else "ranked"] = (time.perf_counter() - t0) * 1e3 / a.steps
+        log(f"ranked {path}: {res['ranked']:.3f} ms/step with compact factors, {res['padded']:.3f} zero-padded "
+            f"to rank {synth.RANK}")
+        out[path] = dict(ms_per_step=round(res["ranked"], 4), padded_ms_per_step=round(res["padded"], 4),
+                         speedup=round(res["padded"] / res["ranked"], 3),
+                         tflops=round(flops / (res["ranked"] / 1e3) / 1e12, 2), adapter_rows=rows)
+        del layer, ws, outs
+        torch.cuda.empty_cache()
+    out["workload"] = (f"one layer's 7 projections with four adapters of ranks {', '.join(map(str, RANKED_RANKS))} "
+                       "(compact factors, lora_proj_ranked) against the same adapters zero-padded to rank 256; "
+                       "prefill: 16384 rows in the 212-segment table of prefill_mixed; decode: 70 rows, 4 x 16 "
+                       "adapter rows and 6 base rows")
+    return out
+
+
 def run_decode(a, dev, hip, grouped=False, q4=False):
     import torch
     w5 = synth.WORKLOADS["suffix"]
@@ -516,7 +598,7 @@ def main(argv=None):
     ap.add_argument("--stack-steps", type=int, default=3, help="timed passes of the 24-layer 32k stack")
     ap.add_argument("--only", choices=("all", "prefill", "mixed", "stack32k", "prefill_9b", "prefill_mixed",
                                        "decode", "decode_grouped",
-                                       "decode_q4", "extract", "peaks"),
+                                       "decode_q4", "ranked", "extract", "peaks"),
                     default="all",
                     help="time one workload only (for profiler runs)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -581,6 +663,7 @@ def main(argv=None):
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
     q4 = (run_decode(a, dev, hip, grouped=True, q4=True)
           if a.only in ("all", "decode", "decode_q4") and not a.no_decode else None)
+    ranked = run_ranked(a, dev) if a.only in ("all", "ranked") else None
     extract = run_extract(a, dev) if a.only in ("all", "extract") else None
     peaks = measure_peaks(dev) if a.only in ("all", "peaks") else None
     hip.close()
@@ -609,7 +692,7 @@ def main(argv=None):
                            parallelism="single GPU"),
                roofline=pre.get("roofline"), cpu_baseline=cpu, decode=decode, decode_grouped=grouped,
                mixed=cfg3, stack32k=st32,
-               prefill_9b=pre9, prefill_mixed=mixed, decode_q4_grouped=q4, extract=extract,
+               prefill_9b=pre9, prefill_mixed=mixed, ranked=ranked, decode_q4_grouped=q4, extract=extract,
                measured_peaks=peaks)
     print(json.dumps(out), flush=True)
     return 0
