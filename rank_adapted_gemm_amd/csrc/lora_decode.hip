@@ -490,9 +490,15 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
             const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + rr * 32 + j * 16 + (lane >> 4) * 4);
             const uint32_t prm = *reinterpret_cast<const uint32_t*>(wq + 1024 + rr * 4);
             const float sc = __uint_as_float(prm << 16);
-            const float zp = float((prm >> 16) & 0xFFu);
+            const float nsz = -sc * float((prm >> 16) & 0xFFu);     // -s z
+            // even codes in the bytes of lo, odd codes in the bytes of hi: one
+            // byte-to-float conversion and one fused multiply-add per code
+            const uint32_t lo = codes & 0x0F0F0F0Fu, hi = (codes >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) a[rg][e] = static_cast<__bf16>(sc * (float((codes >> (4 * e)) & 0xFu) - zp));
+            for (int e = 0; e < 8; ++e) {
+              const uint32_t byte = ((e & 1) ? hi : lo) >> (8 * (e >> 1));
+              a[rg][e] = static_cast<__bf16>(__builtin_fmaf(sc, float(byte & 0xFFu), nsz));
+            }
           }
         } else {
 #pragma unroll

@@ -9,9 +9,10 @@
 // A prefill call is bound by the MFMA pipes, so reading W as 4-bit codes saves
 // nothing there; the codes are expanded into a bf16 copy in the workspace (one
 // HBM pass, a few percent of the call) and the bf16 kernels run unchanged.
-// Each thread turns 8 codes (4 bytes) into 8 bf16 weights (16 bytes), rounded
-// to nearest even, the same rounding the decode kernel applies to its
-// fragments.
+// Each thread turns 8 codes (4 bytes) into 8 bf16 weights (16 bytes): in fp32
+// as fma(s, q, -s z) with -s z rounded once, then rounded to nearest even; the
+// decode kernel computes its fragments the same way, so both paths see the
+// same weights.
 #include <algorithm>
 
 #include "lora_device.h"
@@ -29,12 +30,12 @@ __global__ __launch_bounds__(256) void q4_dequant_kernel(const uint32_t* __restr
     const uint32_t c = codes[i];
     const uint32_t prm = params[(k8 * 8 / 128) * N + n];
     const float s = __uint_as_float(prm << 16);
-    const float z = float((prm >> 16) & 0xFFu);
+    const float nsz = -s * float((prm >> 16) & 0xFFu);     // -s z
     uint32_t o[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const float lo = s * (float((c >> (8 * e)) & 0xFu) - z);
-      const float hi = s * (float((c >> (8 * e + 4)) & 0xFu) - z);
+      const float lo = __builtin_fmaf(s, float((c >> (8 * e)) & 0xFu), nsz);
+      const float hi = __builtin_fmaf(s, float((c >> (8 * e + 4)) & 0xFu), nsz);
       o[e] = pack2(lo, hi);
     }
     w[i] = u32x4{o[0], o[1], o[2], o[3]};
