@@ -334,7 +334,7 @@ def run_prefill(a, dev, hip, name="prefill16k", steps=None, warmup=None):
         + ", ".join(f"{p['name']} {t:.3f}" for p, t in zip(runner.calls, per_proj_ms)))
     roofline = dict(bound="mfma", achieved=round(main_achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(main_achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic_record(),
-                    kernel="main_kernel<Tile<256,256,2,4>, bf16 out>",
+                    kernel="main_kernel<Tile<256,256,2,2>, bf16 out>",
                     launch_avg_ms=round(float(main_ms.mean()), 4),
                     per_projection_ms={p["name"]: round(float(t), 4) for p, t in zip(runner.calls, per_proj_ms)})
     n_calls = len(runner.calls)

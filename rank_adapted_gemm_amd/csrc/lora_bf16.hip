@@ -12,18 +12,23 @@
 //           rows, acc += T_hi B_a^T + T_lo B_a^T over the rank (rows of other
 //           segments read as zero), then one round-to-nearest-even store.
 //
-// Both run the same LDS-staged MFMA K-loop: 32-element K slabs move from
-// global memory straight into a ring of four LDS stages (buffer_load ... lds,
-// 16 bytes per lane, three stages in flight), an XOR swizzle on 16-byte chunks
-// keeps ds_read_b128 conflict-free, and v_mfma_f32_32x32x16_bf16 accumulates in
-// fp32.  The MFMA "A" operand is the weight side (rows n) and
-// "B" is the activation side (rows m), so each lane ends with four consecutive
-// output columns of one row and stores them as one 8-byte write.
+// Both run LDS-staged MFMA K-loops: K slabs move from global memory straight
+// into a ring of LDS stages (buffer_load ... lds, 16 bytes per lane), an XOR
+// swizzle on 16-byte chunks keeps ds_read_b128 conflict-free, and
+// v_mfma_f32_32x32x16_bf16 accumulates in fp32.  The shrink takes 32-element
+// slabs in a ring of four; the main kernel takes 64-element slabs (whole
+// 128-byte lines per row) in a ring of two, with four waves of 128 x 128 that
+// keep their accumulators in AGPRs.  The MFMA "A" operand is the weight side
+// (rows n) and "B" is the activation side (rows m), so each lane ends with
+// four consecutive output columns of one row and stores them as one 8-byte
+// write.
 //
 // Every global access goes through a buffer descriptor sized to its operand:
 // masked or out-of-range loads return zero and out-of-range stores are
 // dropped by the hardware.
 #include "lora_device.h"
+
+#include <type_traits>
 
 namespace lora {
 namespace {
@@ -223,97 +228,215 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, 
   __syncthreads();   // the ring is reused by whatever runs next
 }
 
-// Ping-pong K-loop for 8-wave tiles.  The two waves on each SIMD belong to
-// different groups (waves 0-3 and 4-7), and the groups run one barrier
-// interval apart:
+// ------------------------------------------------------------------ output K-loop
+// Four waves, one per SIMD, each owning a 128 x 128 block of the 256 x 256
+// tile: 16 MFMA tiles whose 256 accumulators per lane live in AGPRs (a wave
+// alone on its SIMD may use 512 registers).  Per k16 substep a wave reads 4 + 4
+// fragments for 16 MFMAs, a third less LDS reading per MFMA than waves of
+// 128 x 64.  Stages are 64 elements of K: every tile row is a 128-byte line,
+// so each load request fetches a whole cache line (with 64-byte rows the same
+// bytes took twice the requests and moved about a quarter less per CU per
+// cycle).  The ring holds two 64 KiB stages.
 //
-//   group 0:  M(0) | C(0) | M(1) | C(1) | ... | C(T-1) | -
-//   group 1:   -   | M(0) | C(0) | M(1) | ... | M(T-1) | C(T-1)
+// A stage is four substeps of 16 MFMAs, each with the next substep's 8
+// fragment reads among its MFMAs.  A wave's 16 loads of a stage go out in
+// four groups of four (one M0 each):
 //
-// so in every interval one wave per SIMD issues nothing but MFMAs on
-// fragments already in registers (C) while the other does the memory work (M):
-// it refills the LDS ring with stage t+D, reads every fragment of stage t into
-// registers (zeroing masked rows and the K tail there, off the MFMA path), and
-// confirms its own loads of stage t+1.  A stage is therefore complete and
-// visible one barrier before either group reads it, and a ring slot is refilled
-// only after both groups have read it.
+//   substep 3 of stage t:    4 MFMAs, then the barrier (stage t+1 landed, no
+//                            wave still reads stage t's slot); groups 0 and 1
+//                            of stage t+2 into that slot
+//   substep 0 of stage t+1:  groups 2 and 3, after its 8th and 12th MFMA
+//
+// Spreading them so (rather than all 16 right after the barrier) keeps the
+// texture path from backing up into the MFMA stream, and the MFMAs issued
+// before the barrier cover a little of the waves' skew there.
+constexpr int BKW = 64;             // K elements per stage of the output loop
+constexpr int ROWW = BKW * 2;       // bytes per tile row per stage
+
+// 16-byte chunk c of 128-byte row r sits at slot c ^ ((r >> 1) & 7): the 16
+// lanes that a ds_read_b128 serves per cycle read one chunk of 16 consecutive
+// rows, which this spreads over all 64 banks.
+__device__ __forceinline__ int lds_off_w(int r, int c) { return r * ROWW + ((c ^ ((r >> 1) & 7)) << 4); }
+__device__ __forceinline__ bf16x8 read_frag_w(const char* base, int r, int c) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lds_off_w(r, c)));
+}
+
+template <class C>
+struct WideRing {
+  static constexpr int STAGE = (C::TN + C::TM) * ROWW;   // 64 KiB for 256 x 256
+  static constexpr int PW = STAGE / 1024 / C::NW;        // 8-row loads per wave per stage
+  static_assert(PW == 16 && (C::TN / 8) % PW == 0, "four groups of four loads, all on one side");
+};
+
+// K-loop over `ntiles` stages; src(t, ws, xs, k0) names the operands and K
+// offset of stage t, with each side's row stride the same in every stage.
+// Chunks at or past kdim enter the MFMAs as zero; with MASK_ROWS so do the
+// activation rows whose bit in `keep` is clear.
 template <class C, bool MASK_ROWS, class Src>
-__device__ __forceinline__ void k_loop_pingpong(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src,
-                                                char* smem, int tid, int wn, int wm, uint32_t keep = 0) {
-  static_assert(C::NW == 8, "ping-pong needs two waves per SIMD");
-  constexpr int D = NSTAGE - 1;
+__device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src, char* smem,
+                                            int tid, int wn, int wm, uint32_t keep = 0) {
+  static_assert(C::NW == 4 && C::FN == 4 && C::FM == 4, "four waves of 128 x 128");
+  using R = WideRing<C>;
   if (ntiles <= 0) return;
-  const int lane = tid & 63, wave = tid >> 6;
-  const bool trailing = wave >= 4;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
-#pragma unroll
-  for (int p = 0; p < D; ++p) {
-    if (p < ntiles) {
-      Side ws, xs;
-      int k0;
-      src(p, ws, xs, k0);
-      issue_stage<C>(smem + p * C::STAGE, ws, xs, k0, wave, lane);
-    }
-  }
-  wait_stages<C::PW>(min(D, ntiles) - 1);   // stage 0 complete
-  __syncthreads();
-  if (trailing) __syncthreads();
-  bf16x8 fa[BK / 16][C::FN], fb[BK / 16][C::FM];
-  for (int t = 0; t < ntiles; ++t) {
-    // ---- M(t): this stage's fragment reads first, then the loads that refill
-    // the slot freed one step ago (reads queued behind the LDS-DMA writes cost
-    // 2% on the 16k projections)
-    __builtin_amdgcn_sched_barrier(0);
-    Side ws, xs;
+
+  // A wave's loads all lie on one side.  Each lane's offsets within a stage
+  // (row in the tile, swizzled chunk, group bias) are fixed; a stage adds the
+  // uniform row0 * stride + 2 k0.
+  const bool wside = wave * R::PW * 8 < C::TN;
+  uint32_t lb[R::PW];
+  {
+    Side w, x;
     int k0;
-    src(t, ws, xs, k0);
-    const char* wt = smem + (t % NSTAGE) * C::STAGE;
-    const char* xt = wt + C::TN * ROW_BYTES;
+    src(0, w, x, k0);
+    const uint32_t ld = wside ? w.ld_bytes : x.ld_bytes;
 #pragma unroll
-    for (int s = 0; s < BK / 16; ++s) {
-      const int c = 2 * s + (lane >> 5);
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i) fa[s][i] = read_frag(wt, wrow + i * 32 + (lane & 31), c);
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j) fb[s][j] = read_frag(xt, xrow + j * 32 + (lane & 31), c);
-      if (k0 + BK > kdim && k0 + c * 8 >= kdim) {   // the first test is uniform: only tail stages pay
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i) fa[s][i] = bf16x8{};
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j) fb[s][j] = bf16x8{};
-      }
-      if constexpr (MASK_ROWS) {   // activation row j of this lane enters only if bit j of keep is set
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j)
-          if (!((keep >> j) & 1u)) fb[s][j] = bf16x8{};
-      }
+    for (int q = 0; q < R::PW; ++q) {
+      const int r = (wave * R::PW + q) * 8 + (lane >> 3) - (wside ? 0 : C::TN);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
+      lb[q] = uint32_t(r) * ld + uint32_t(c) * 16u - 1024u * uint32_t(q & 3);
     }
-    if (t + D < ntiles) {
-      Side ws2, xs2;
-      int k2;
-      src(t + D, ws2, xs2, k2);
-      issue_stage<C>(smem + ((t + D) % NSTAGE) * C::STAGE, ws2, xs2, k2, wave, lane);
-    }
-    // own loads of stage t+1 complete; loads of later stages may stay in flight
-    wait_stages<C::PW>(min(t + D, ntiles - 1) - (t + 1));
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-    // ---- C(t), at raised wave priority: where the two waves of a SIMD meet,
-    // the one in its multiply phase issues first (1.4% faster on the 16k
-    // projections)
-    __builtin_amdgcn_s_setprio(1);
-#pragma unroll
-    for (int s = 0; s < BK / 16; ++s)
-#pragma unroll
-      for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[s][i], fb[s][j], acc[i][j], 0, 0, 0);
-    __builtin_amdgcn_s_setprio(0);
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
   }
-  if (!trailing) __syncthreads();
+  struct Dest {   // where a stage's loads go
+    i32x4 res;
+    uint32_t add;
+    char* slot;
+  };
+  auto dest = [&](int t) __attribute__((always_inline)) {
+    Side w, x;
+    int k0;
+    src(t, w, x, k0);
+    const Side& sd = wside ? w : x;
+    return Dest{sd.res, uint32_t(sd.row0) * sd.ld_bytes + uint32_t(k0) * 2u, smem + (t & 1) * R::STAGE};
+  };
+  auto group = [&](const Dest& d, int g) __attribute__((always_inline)) {
+    dma16x4_biased(d.res, lb[4 * g] + d.add, lb[4 * g + 1] + d.add, lb[4 * g + 2] + d.add, lb[4 * g + 3] + d.add,
+                   lds_addr(d.slot) + uint32_t(wave * R::PW + 4 * g) * 1024u);
+  };
+  {
+    const Dest d0 = dest(0);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) group(d0, g);
+  }
+  if (ntiles > 1) {
+    const Dest d1 = dest(1);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) group(d1, g);
+    wait_vm<R::PW>();   // own loads of stage 0
+  } else {
+    wait_vm<0>();
+  }
+  __syncthreads();
+
+  bf16x8 fa[2][C::FN], fb[2][C::FM];
+  const int rl = lane & 31, ch = lane >> 5;
+  {
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i) fa[0][i] = read_frag_w(smem, wrow + i * 32 + rl, ch);
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) fb[0][j] = read_frag_w(smem + C::TN * ROWW, xrow + j * 32 + rl, ch);
+  }
+  // chunks at or past kdim and masked activation rows enter as zero
+  auto fix = [&](int k0, int s, int buf) __attribute__((always_inline)) {
+    if (k0 + (2 * s + ch) * 8 >= kdim) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) fa[buf][i] = bf16x8{};
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) fb[buf][j] = bf16x8{};
+    }
+    if constexpr (MASK_ROWS) {
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j)
+        if (!((keep >> j) & 1u)) fb[buf][j] = bf16x8{};
+    }
+  };
+  auto mfma = [&](int buf, int i, int j) __attribute__((always_inline)) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+
+  Dest held{};          // stage t+1's groups 2 and 3, issued in substep 0 of stage t
+  bool held_live = false;
+  auto iter = [&](int t, auto checked) __attribute__((always_inline)) {
+    constexpr bool CHECKED = decltype(checked)::value;
+    int k0 = 0;
+    if constexpr (CHECKED) {
+      Side w, x;
+      src(t, w, x, k0);
+    }
+    const bool live = t + 2 < ntiles;
+    Dest next{};
+    auto substep = [&](auto sc) __attribute__((always_inline)) {
+      constexpr int s = decltype(sc)::value;
+      constexpr int buf = s & 1, ns = s < 3 ? s + 1 : 0, nb = (s + 1) & 1;
+      __builtin_amdgcn_sched_barrier(0);
+      if constexpr (CHECKED) fix(k0, s, buf);
+      // the next substep's fragments: this stage's, or stage t+1's first (past
+      // the last stage a stale slot, never used)
+      const char* nx = smem + ((s < 3 ? t : t + 1) & 1) * R::STAGE;
+      auto rd = [&](int g) __attribute__((always_inline)) {
+        fa[nb][g] = read_frag_w(nx, wrow + g * 32 + rl, 2 * ns + ch);
+        fb[nb][g] = read_frag_w(nx + C::TN * ROWW, xrow + g * 32 + rl, 2 * ns + ch);
+      };
+      auto chunk = [&](auto gc) __attribute__((always_inline)) {
+        constexpr int g = decltype(gc)::value;
+        if constexpr (s == 3 && g == 0) {
+          mfma(buf, 0, 0);
+          mfma(buf, 0, 1);
+          mfma(buf, 0, 2);
+          mfma(buf, 0, 3);
+          __builtin_amdgcn_sched_barrier(0);
+          // own loads of stage t+1 landed; after the barrier every wave's
+          // have, and every wave has read all of stage t
+          wait_vm<0>();
+          __syncthreads();
+          __builtin_amdgcn_sched_barrier(0);
+          rd(0);
+          next = dest(live ? t + 2 : t);
+          if (live) group(next, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          return;
+        }
+        mfma(buf, g, 0);
+        fa[nb][g] = read_frag_w(nx, wrow + g * 32 + rl, 2 * ns + ch);
+        mfma(buf, g, 1);
+        fb[nb][g] = read_frag_w(nx + C::TN * ROWW, xrow + g * 32 + rl, 2 * ns + ch);
+        mfma(buf, g, 2);
+        mfma(buf, g, 3);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (s == 3 && g == 1) {
+          if (live) group(next, 1);
+        }
+        if constexpr (s == 0 && g >= 2) {
+          if (held_live) group(held, g);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      chunk(std::integral_constant<int, 0>{});
+      chunk(std::integral_constant<int, 1>{});
+      chunk(std::integral_constant<int, 2>{});
+      chunk(std::integral_constant<int, 3>{});
+    };
+    substep(std::integral_constant<int, 0>{});
+    substep(std::integral_constant<int, 1>{});
+    substep(std::integral_constant<int, 2>{});
+    substep(std::integral_constant<int, 3>{});
+    held = next;
+    held_live = live;
+  };
+  // the K tail can only fall in the last stage of the base product; the
+  // expand (MASK_ROWS) checks every stage
+  int t = 0;
+  if constexpr (!MASK_ROWS) {
+    for (; t + 1 < ntiles; ++t) iter(t, std::false_type{});
+  }
+  for (; t < ntiles; ++t) iter(t, std::true_type{});
+  __syncthreads();   // the ring is reused by whatever runs next
 }
 
 // ------------------------------------------------------------------ scheduling
@@ -417,9 +540,9 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
 
 // ------------------------------------------------------------------ main
 template <class C, bool F32_OUT>
-__global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, AdapterTable at, int has_adapter,
-                                                     int ntn, int ntm) {
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
+__global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) void main_kernel(
+    ProjArgs p, SegTable st, AdapterTable at, int has_adapter, int ntn, int ntm) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * WideRing<C>::STAGE];
   __shared__ int8_t row_adapter[C::TM];   // adapter named by each row of the tile, -1 for none
   int tn, tm;
   tile_of_block(blockIdx.x, ntn, ntm, tn, tm);
@@ -446,9 +569,9 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
   {
     const Side ws{make_rsrc_words(p.W, p.w_bytes), uint32_t(p.K) * 2u, n0, 0, p.N};
     const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0, 0, p.M};
-    const int nk = (p.K + BK - 1) / BK;
-    auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BK; };
-    k_loop_pingpong<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
+    const int nk = (p.K + BKW - 1) / BKW;
+    auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BKW; };
+    k_loop_wide<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
   }
 
   // expand: for each adapter that rows of the tile name, stages alternate
@@ -478,9 +601,9 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
       const Side bs{make_rsrc_words(at.B[a], at.b_bytes[a]), ld, n0, 0, p.N};
       const Side th{tres, tld, m0, 0, 0};
       const Side tl{tres, tld, lo_row0, 0, 0};
-      const int nr = 2 * ((ra + BK - 1) / BK);
-      auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
-      k_loop_pingpong<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
+      const int nr = 2 * ((ra + BKW - 1) / BKW);
+      auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BKW; };
+      k_loop_wide<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
     }
   }
 
@@ -538,12 +661,11 @@ __global__ __launch_bounds__(C::NT) void main_kernel(ProjArgs p, SegTable st, Ad
   }
 }
 
-// Tile choices.  Output: 256x256 tiles, eight waves of 128 (n) x 64 (m): two
-// waves per SIMD, so one wave's MFMAs cover the other's LDS waits and
-// barriers; 128 fp32 accumulators per lane, 128 KiB of LDS for the ring.
+// Tile choices.  Output: 256x256 tiles, four waves of 128 x 128, one per SIMD,
+// 256 fp32 accumulators per lane (in AGPRs), 128 KiB of LDS for the ring.
 // Shrink: 128x128 tiles, so a 256-wide rank still gives two blocks per row
 // tile.  (Batches of at most 128 rows take the decode kernel.)
-using MainBig = Tile<256, 256, 2, 4>;
+using MainBig = Tile<256, 256, 2, 2>;
 using ShrinkBig = Tile<128, 128, 2, 2>;
 
 template <class C>

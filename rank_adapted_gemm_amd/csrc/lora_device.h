@@ -115,6 +115,22 @@ __device__ __forceinline__ void dma16_group(const i32x4& res, const uint32_t (&v
   }
 }
 
+// Four wave-wide 16-byte global -> LDS loads under one M0, landing at lds_addr
+// + 1024 i; voff[i] already carries the bias -1024 i that the instruction
+// offsets undo (a loop that keeps its offsets across stages biases them once).
+__device__ __forceinline__ void dma16x4_biased(const i32x4& res, uint32_t v0, uint32_t v1, uint32_t v2, uint32_t v3,
+                                               uint32_t lds_addr) {
+  const i32x4 r{__builtin_amdgcn_readfirstlane(res[0]), __builtin_amdgcn_readfirstlane(res[1]),
+                __builtin_amdgcn_readfirstlane(res[2]), __builtin_amdgcn_readfirstlane(res[3])};
+  asm volatile("s_mov_b32 m0, %4\n\t"
+               "buffer_load_dwordx4 %0, %5, 0 offen lds\n\t"
+               "buffer_load_dwordx4 %1, %5, 0 offen offset:1024 lds\n\t"
+               "buffer_load_dwordx4 %2, %5, 0 offen offset:2048 lds\n\t"
+               "buffer_load_dwordx4 %3, %5, 0 offen offset:3072 lds"
+               : : "v"(v0), "v"(v1), "v"(v2), "v"(v3), "s"(__builtin_amdgcn_readfirstlane(lds_addr)), "s"(r)
+               : "memory");
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() { asm volatile("s_waitcnt vmcnt(%0)" : : "n"(N) : "memory"); }
 
