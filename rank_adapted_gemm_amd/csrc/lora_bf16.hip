@@ -357,8 +357,9 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
 
   Dest held{};          // stage t+1's groups 2 and 3, issued in substep 0 of stage t
   bool held_live = false;
-  auto iter = [&](int t, auto checked) __attribute__((always_inline)) {
+  auto iter = [&](int t, auto checked, auto parity) __attribute__((always_inline)) {
     constexpr bool CHECKED = decltype(checked)::value;
+    constexpr int P = decltype(parity)::value;   // t & 1
     int k0 = 0;
     if constexpr (CHECKED) {
       Side w, x;
@@ -373,7 +374,7 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
       if constexpr (CHECKED) fix(k0, s, buf);
       // the next substep's fragments: this stage's, or stage t+1's first (past
       // the last stage a stale slot, never used)
-      const char* nx = smem + ((s < 3 ? t : t + 1) & 1) * R::STAGE;
+      const char* nx = smem + ((s < 3 ? P : P + 1) & 1) * R::STAGE;
       auto rd = [&](int g) __attribute__((always_inline)) {
         fa[nb][g] = read_frag_w(nx, wrow + g * 32 + rl, 2 * ns + ch);
         fb[nb][g] = read_frag_w(nx + C::TN * ROWW, xrow + g * 32 + rl, 2 * ns + ch);
@@ -429,13 +430,24 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
     held = next;
     held_live = live;
   };
-  // the K tail can only fall in the last stage of the base product; the
-  // expand (MASK_ROWS) checks every stage
+  // Stages go in pairs, so that the ring slot a fragment read addresses is a
+  // compile-time constant (its address then needs no per-stage arithmetic).
+  // The K tail can only fall in the last stage of the base product; the
+  // expand (MASK_ROWS) checks every stage.
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
   int t = 0;
   if constexpr (!MASK_ROWS) {
-    for (; t + 1 < ntiles; ++t) iter(t, std::false_type{});
+    for (; t + 2 < ntiles; t += 2) {
+      iter(t, std::false_type{}, P0{});
+      iter(t + 1, std::false_type{}, P1{});
+    }
   }
-  for (; t < ntiles; ++t) iter(t, std::true_type{});
+  for (; t + 1 < ntiles; t += 2) {
+    iter(t, std::true_type{}, P0{});
+    iter(t + 1, std::true_type{}, P1{});
+  }
+  if (t < ntiles) iter(t, std::true_type{}, P0{});
   __syncthreads();   // the ring is reused by whatever runs next
 }
 
