@@ -15,10 +15,10 @@
 // Both run LDS-staged MFMA K-loops: K slabs move from global memory straight
 // into a ring of LDS stages (buffer_load ... lds, 16 bytes per lane), an XOR
 // swizzle on 16-byte chunks keeps ds_read_b128 conflict-free, and
-// v_mfma_f32_32x32x16_bf16 accumulates in fp32.  The shrink takes 32-element
-// slabs in a ring of four; the main kernel takes 64-element slabs (whole
-// 128-byte lines per row) in a ring of two, with four waves of 128 x 128 that
-// keep their accumulators in AGPRs.  The MFMA "A" operand is the weight side
+// v_mfma_f32_32x32x16_bf16 accumulates in fp32.  Slabs are 64 elements of K
+// (one whole 128-byte line per row); the shrink keeps a ring of four, the main
+// kernel a ring of two, with four waves of 128 x 128 that keep their
+// accumulators in AGPRs.  The MFMA "A" operand is the weight side
 // (rows n) and "B" is the activation side (rows m), so each lane ends with
 // four consecutive output columns of one row and stores them as one 8-byte
 // write.
@@ -33,9 +33,13 @@
 namespace lora {
 namespace {
 
-constexpr int BK = 32;          // K elements per LDS stage (64 bytes per tile row)
+// K elements per LDS stage: 128 bytes per tile row, so every row of a stage is
+// one whole cache line and each load request fetches a full line (with 64-byte
+// rows the same bytes took twice the requests and moved about a quarter less
+// per CU per cycle).
+constexpr int BK = 64;
 constexpr int ROW_BYTES = BK * 2;
-constexpr int NSTAGE = 4;       // LDS ring depth; NSTAGE - 1 stages are in flight
+constexpr int NSTAGE = 4;       // LDS ring depth of the shrink; NSTAGE - 1 stages are in flight
 
 // One operand of a K-loop: rows of a row-major bf16 matrix whose reduction
 // index is contiguous.  Tile row i is global row row0 + i.  Rows past the
@@ -57,18 +61,17 @@ struct Tile {
   static constexpr int FN = TN / WN / 32;        // MFMA tiles per wave along n
   static constexpr int FM = TM / WM / 32;        // ... along m
   static constexpr int STAGE = (TN + TM) * ROW_BYTES;
-  static constexpr int GROUPS = STAGE / 1024;    // 16-row groups: one wave-wide 16-byte load each
+  static constexpr int GROUPS = STAGE / 1024;    // 8-row groups: one wave-wide 16-byte load each
   static constexpr int PW = GROUPS / NW;         // loads per wave per stage
   static_assert(FN >= 1 && FM >= 1, "wave tile smaller than one MFMA tile");
   static_assert(TN % 16 == 0 && TM % 16 == 0 && GROUPS % NW == 0, "row groups must split evenly over waves");
 };
 
-// Chunk c (16 bytes) of tile row r lives at slot c ^ ((r >> 2) & 3).  The LDS
-// has 64 four-byte banks and serves 16 lanes of a ds_read_b128 per cycle;
-// those lanes read one chunk of 16 consecutive rows.  A 64-byte row covers a
-// quarter of the banks, and the XOR gives the four rows that share a quarter
-// four distinct slots, so no two lanes of a cycle share a bank.
-__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ ((r >> 2) & 3)) << 4); }
+// 16-byte chunk c of 128-byte row r sits at slot c ^ ((r >> 1) & 7).  The
+// LDS has 64 four-byte banks and serves 16 lanes of a ds_read_b128 per cycle;
+// those lanes read one chunk of 16 consecutive rows, which the XOR spreads over
+// all 64 banks.
+__device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ ((r >> 1) & 7)) << 4); }
 
 // Wait until at most `stages` later stages of PW loads each are still in flight.
 template <int PW>
@@ -80,7 +83,7 @@ __device__ __forceinline__ void wait_stages(int stages) {
   else wait_vm<0>();
 }
 
-// A wave's PW loads of a stage are consecutive 16-row groups of one side (the
+// A wave's PW loads of a stage are consecutive 8-row groups of one side (the
 // weight rows come first and fill whole waves), so they go out in groups of up
 // to four under one M0 value.  GATHER: the activation side's loads start at
 // the per-lane byte offsets gx[] (gather_offsets).  A row with no X row behind
@@ -92,20 +95,20 @@ constexpr uint32_t kGatherMasked = 0x80001000u;
 template <class C, bool GATHER = false>
 __device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane,
                                             const uint32_t* gx = nullptr) {
-  static_assert((C::TN / 16) % C::PW == 0, "a wave's groups must lie on one side");
+  static_assert((C::TN / 8) % C::PW == 0, "a wave's groups must lie on one side");
   constexpr int NG = C::PW < 4 ? C::PW : 4;
   static_assert(C::PW % NG == 0, "groups of loads must split evenly");
   const uint32_t base = lds_addr(stage);
-  const int g0 = wave * C::PW;                      // first 16-row group of the wave (uniform)
-  const bool wside = g0 * 16 < C::TN;
+  const int g0 = wave * C::PW;                      // first 8-row group of the wave (uniform)
+  const bool wside = g0 * 8 < C::TN;
   const Side& sd = wside ? ws : xs;
 #pragma unroll
   for (int q = 0; q < C::PW; q += NG) {
     uint32_t off[NG];
 #pragma unroll
     for (int i = 0; i < NG; ++i) {
-      const int r = (g0 + q + i) * 16 + (lane >> 2) - (wside ? 0 : C::TN);
-      const int c = (lane & 3) ^ ((r >> 2) & 3);
+      const int r = (g0 + q + i) * 8 + (lane >> 3) - (wside ? 0 : C::TN);
+      const int c = (lane & 7) ^ ((r >> 1) & 7);
       if (GATHER && !wside) {
         off[i] = gx[q + i] + uint32_t(k0) * 2u;
       } else {
@@ -125,8 +128,8 @@ __device__ __forceinline__ void gather_offsets(uint32_t (&gx)[C::PW], const int*
   const int g0 = wave * C::PW;
 #pragma unroll
   for (int i = 0; i < C::PW; ++i) {
-    const int r = (g0 + i) * 16 + (lane >> 2) - C::TN;
-    const int c = (lane & 3) ^ ((r >> 2) & 3);
+    const int r = (g0 + i) * 8 + (lane >> 3) - C::TN;
+    const int c = (lane & 7) ^ ((r >> 1) & 7);
     const int row = r >= 0 ? xrows[r] : -1;
     gx[i] = row >= 0 ? uint32_t(row) * ld_bytes + uint32_t(c) * 16u : kGatherMasked;
   }
@@ -136,7 +139,7 @@ __device__ __forceinline__ bf16x8 read_frag(const char* base, int r, int c) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lds_off(r, c)));
 }
 
-// acc += (weight tile) x (activation tile)^T over one 32-wide stage (two k16
+// acc += (weight tile) x (activation tile)^T over one stage (BK / 16 k16
 // substeps).  MASK_ROWS zeroes activation rows outside [lo, hi); TAIL zeroes
 // the chunks at or past kdim on both sides.
 template <class C, bool MASK_ROWS, bool TAIL>
@@ -233,10 +236,7 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, 
 // tile: 16 MFMA tiles whose 256 accumulators per lane live in AGPRs (a wave
 // alone on its SIMD may use 512 registers).  Per k16 substep a wave reads 4 + 4
 // fragments for 16 MFMAs, a third less LDS reading per MFMA than waves of
-// 128 x 64.  Stages are 64 elements of K: every tile row is a 128-byte line,
-// so each load request fetches a whole cache line (with 64-byte rows the same
-// bytes took twice the requests and moved about a quarter less per CU per
-// cycle).  The ring holds two 64 KiB stages.
+// 128 x 64.  The ring holds two 64 KiB stages of BK = 64.
 //
 // A stage is four substeps of 16 MFMAs, each with the next substep's 8
 // fragment reads among its MFMAs.  A wave's 16 loads of a stage go out in
@@ -245,26 +245,15 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, 
 //   substep 3 of stage t:    4 MFMAs, then the barrier (stage t+1 landed, no
 //                            wave still reads stage t's slot); groups 0 and 1
 //                            of stage t+2 into that slot
-//   substep 0 of stage t+1:  groups 2 and 3, after its 8th and 12th MFMA
+//   substep 0 of stage t+1:  groups 2 and 3, after its 12th and 16th MFMA
 //
 // Spreading them so (rather than all 16 right after the barrier) keeps the
 // texture path from backing up into the MFMA stream, and the MFMAs issued
 // before the barrier cover a little of the waves' skew there.
-constexpr int BKW = 64;             // K elements per stage of the output loop
-constexpr int ROWW = BKW * 2;       // bytes per tile row per stage
-
-// 16-byte chunk c of 128-byte row r sits at slot c ^ ((r >> 1) & 7): the 16
-// lanes that a ds_read_b128 serves per cycle read one chunk of 16 consecutive
-// rows, which this spreads over all 64 banks.
-__device__ __forceinline__ int lds_off_w(int r, int c) { return r * ROWW + ((c ^ ((r >> 1) & 7)) << 4); }
-__device__ __forceinline__ bf16x8 read_frag_w(const char* base, int r, int c) {
-  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lds_off_w(r, c)));
-}
-
 template <class C>
 struct WideRing {
-  static constexpr int STAGE = (C::TN + C::TM) * ROWW;   // 64 KiB for 256 x 256
-  static constexpr int PW = STAGE / 1024 / C::NW;        // 8-row loads per wave per stage
+  static constexpr int STAGE = C::STAGE;   // 64 KiB for 256 x 256
+  static constexpr int PW = C::PW;         // 8-row loads per wave per stage
   static_assert(PW == 16 && (C::TN / 8) % PW == 0, "four groups of four loads, all on one side");
 };
 
@@ -333,9 +322,9 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
   const int rl = lane & 31, ch = lane >> 5;
   {
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i) fa[0][i] = read_frag_w(smem, wrow + i * 32 + rl, ch);
+    for (int i = 0; i < C::FN; ++i) fa[0][i] = read_frag(smem, wrow + i * 32 + rl, ch);
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) fb[0][j] = read_frag_w(smem + C::TN * ROWW, xrow + j * 32 + rl, ch);
+    for (int j = 0; j < C::FM; ++j) fb[0][j] = read_frag(smem + C::TN * ROW_BYTES, xrow + j * 32 + rl, ch);
   }
   // chunks at or past kdim and masked activation rows enter as zero
   auto fix = [&](int k0, int s, int buf) __attribute__((always_inline)) {
@@ -376,8 +365,8 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
       // the last stage a stale slot, never used)
       const char* nx = smem + ((s < 3 ? P : P + 1) & 1) * R::STAGE;
       auto rd = [&](int g) __attribute__((always_inline)) {
-        fa[nb][g] = read_frag_w(nx, wrow + g * 32 + rl, 2 * ns + ch);
-        fb[nb][g] = read_frag_w(nx + C::TN * ROWW, xrow + g * 32 + rl, 2 * ns + ch);
+        fa[nb][g] = read_frag(nx, wrow + g * 32 + rl, 2 * ns + ch);
+        fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
       };
       auto chunk = [&](auto gc) __attribute__((always_inline)) {
         constexpr int g = decltype(gc)::value;
@@ -399,9 +388,9 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
           return;
         }
         mfma(buf, g, 0);
-        fa[nb][g] = read_frag_w(nx, wrow + g * 32 + rl, 2 * ns + ch);
+        fa[nb][g] = read_frag(nx, wrow + g * 32 + rl, 2 * ns + ch);
         mfma(buf, g, 1);
-        fb[nb][g] = read_frag_w(nx + C::TN * ROWW, xrow + g * 32 + rl, 2 * ns + ch);
+        fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
         mfma(buf, g, 2);
         mfma(buf, g, 3);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
@@ -581,13 +570,13 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   {
     const Side ws{make_rsrc_words(p.W, p.w_bytes), uint32_t(p.K) * 2u, n0, 0, p.N};
     const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0, 0, p.M};
-    const int nk = (p.K + BKW - 1) / BKW;
-    auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BKW; };
+    const int nk = (p.K + BK - 1) / BK;
+    auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BK; };
     k_loop_wide<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
   }
 
   // expand: for each adapter that rows of the tile name, stages alternate
-  // T_hi and T_lo against the same 32-wide slab of B_a, with the rows that
+  // T_hi and T_lo against the same 64-wide slab of B_a, with the rows that
   // name another adapter or none masked to zero: one pass per adapter however
   // many segments it has in the tile (each row's own adapter adds its term in
   // one pass, the other passes add exact zeros).  The tile's slice reads its
@@ -613,8 +602,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       const Side bs{make_rsrc_words(at.B[a], at.b_bytes[a]), ld, n0, 0, p.N};
       const Side th{tres, tld, m0, 0, 0};
       const Side tl{tres, tld, lo_row0, 0, 0};
-      const int nr = 2 * ((ra + BKW - 1) / BKW);
-      auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BKW; };
+      const int nr = 2 * ((ra + BK - 1) / BK);
+      auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
       k_loop_wide<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
     }
   }
