@@ -320,6 +320,14 @@ size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, 
  * ("invalid" for arguments lora_proj would reject).  A pure function of its arguments. */
 const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_dtype dtype);
 
+/* Activation rows per output tile of the prefill output kernel for this shape: 256, 192 or 128
+ * (the tile is always 256 output columns wide).  The kernel runs one tile per CU in whole waves
+ * over the 256 CUs, so a batch of 2,054 rows, 9 tiles of 256 rows by 20 column tiles (0.70 of a
+ * wave), takes 11 tiles of 192 rows instead (one wave of shorter tiles).  0 where lora_proj does
+ * not take the prefill path (at most 128 rows, the f32 test mode) or would reject the arguments.
+ * A pure function of its arguments. */
+int32_t lora_proj_tile_rows(int64_t M, int64_t N, int64_t K, lora_dtype dtype);
+
 /*
  * lora_proj_noalloc — lora_proj for callers that cannot allocate memory.
  *

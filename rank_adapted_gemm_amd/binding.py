@@ -24,7 +24,7 @@ MAX_SLICES, SLICE_ALIGN = 4, 256
 WORKSPACE_COUNTER_BYTES = 65536   # zero-filled counter area at the start of every workspace
 EXPORTS = ("lora_proj", "lora_proj_ex", "lora_proj_multi", "lora_proj_sliced", "lora_proj_q4",
            "lora_proj_workspace_bytes", "lora_proj_sliced_workspace_bytes", "lora_proj_q4_workspace_bytes",
-           "lora_proj_path", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes",
+           "lora_proj_path", "lora_proj_tile_rows", "lora_status_string", "lora_extract", "lora_extract_workspace_bytes",
            "lora_probe_mfma_bf16", "lora_probe_read", "lora_workspace_status", "lora_debug_handover_fault",
            "lora_decode_plan_describe", "lora_proj_noalloc", "lora_proj_ranked")
 NOALLOC_SCRATCH_BYTES = 64 << 20   # the device array lora_proj_noalloc uses instead of a workspace
@@ -86,6 +86,8 @@ def load():
     lib.lora_proj_workspace_bytes.restype = sz
     lib.lora_proj_path.argtypes = [i64, i64, i64, i32, ctypes.c_int]
     lib.lora_proj_path.restype = ctypes.c_char_p
+    lib.lora_proj_tile_rows.argtypes = [i64, i64, i64, ctypes.c_int]
+    lib.lora_proj_tile_rows.restype = i32
     lib.lora_status_string.argtypes = [ctypes.c_int]
     lib.lora_status_string.restype = ctypes.c_char_p
     lib.lora_proj_noalloc.argtypes = lib.lora_proj.argtypes[:15] + [vp]
@@ -255,6 +257,11 @@ def extract(W_adapted, W_base, rank, omega, power_iters=2, stream=None):
 
 def path(M: int, N: int, K: int, rank: int, dtype: str = "bf16") -> str:
     return load().lora_proj_path(M, N, K, rank, DTYPES[dtype]).decode()
+
+
+def tile_rows(M: int, N: int, K: int, dtype: str = "bf16") -> int:
+    """Activation rows per prefill output tile for this shape (0 off the prefill path)."""
+    return int(load().lora_proj_tile_rows(M, N, K, DTYPES[dtype]))
 
 
 def lora_proj_raw(X, seg_starts, seg_adapter, W, A, B, rank, scale, Y, M, N, K, dtype,

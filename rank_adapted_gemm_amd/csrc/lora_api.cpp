@@ -189,6 +189,11 @@ const char* lora_proj_path(int64_t M, int64_t N, int64_t K, int32_t rank, lora_d
   return small_m(M) ? "decode" : "prefill";
 }
 
+int32_t lora_proj_tile_rows(int64_t M, int64_t N, int64_t K, lora_dtype dtype) {
+  if (check_shape(M, N, K, dtype) != LORA_OK || dtype == LORA_F32 || small_m(M)) return 0;
+  return lora::main_tile_rows(int(M), int(N));
+}
+
 }  // extern "C"
 
 namespace {

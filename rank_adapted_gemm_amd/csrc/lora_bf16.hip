@@ -252,9 +252,12 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, 
 // before the barrier cover a little of the waves' skew there.
 template <class C>
 struct WideRing {
-  static constexpr int STAGE = C::STAGE;   // 64 KiB for 256 x 256
-  static constexpr int PW = C::PW;         // 8-row loads per wave per stage
-  static_assert(PW == 16 && (C::TN / 8) % PW == 0, "four groups of four loads, all on one side");
+  static constexpr int STAGE = C::STAGE;        // 64 KiB for 256 x 256
+  // 8-row loads per stage of each weight-side wave (waves 0, 1) and each
+  // activation-side wave (waves 2, 3): four groups of four, or fewer on the
+  // activation side of a shorter tile
+  static constexpr int PWW = C::TN / 16, PWX = C::TM / 16;
+  static_assert(C::NW == 4 && PWW == 16 && PWX % 4 == 0 && PWX >= 8 && PWX <= 16, "load groups of four");
 };
 
 // K-loop over `ntiles` stages; src(t, ws, xs, k0) names the operands and K
@@ -264,25 +267,27 @@ struct WideRing {
 template <class C, bool MASK_ROWS, class Src>
 __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src, char* smem,
                                             int tid, int wn, int wm, uint32_t keep = 0) {
-  static_assert(C::NW == 4 && C::FN == 4 && C::FM == 4, "four waves of 128 x 128");
+  static_assert(C::NW == 4 && C::FN == 4 && C::FM >= 2 && C::FM <= 4, "four waves of 128 x (64, 96 or 128)");
   using R = WideRing<C>;
   if (ntiles <= 0) return;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
 
-  // A wave's loads all lie on one side.  Each lane's offsets within a stage
-  // (row in the tile, swizzled chunk, group bias) are fixed; a stage adds the
-  // uniform row0 * stride + 2 k0.
-  const bool wside = wave * R::PW * 8 < C::TN;
-  uint32_t lb[R::PW];
+  // Waves 0 and 1 load the weight rows, waves 2 and 3 the activation rows.
+  // Each lane's offsets within a stage (row in the tile, swizzled chunk, group
+  // bias) are fixed; a stage adds the uniform row0 * stride + 2 k0.
+  const bool wside = wave < 2;
+  const int q0 = wside ? wave * R::PWW : C::TN / 8 + (wave - 2) * R::PWX;   // first 8-row load of the wave
+  const int ngroups = wside ? R::PWW / 4 : R::PWX / 4;
+  uint32_t lb[R::PWW];
   {
     Side w, x;
     int k0;
     src(0, w, x, k0);
     const uint32_t ld = wside ? w.ld_bytes : x.ld_bytes;
 #pragma unroll
-    for (int q = 0; q < R::PW; ++q) {
-      const int r = (wave * R::PW + q) * 8 + (lane >> 3) - (wside ? 0 : C::TN);
+    for (int q = 0; q < R::PWW; ++q) {   // past the activation side's loads: never used
+      const int r = (q0 + q) * 8 + (lane >> 3) - (wside ? 0 : C::TN);
       const int c = (lane & 7) ^ ((r >> 1) & 7);
       lb[q] = uint32_t(r) * ld + uint32_t(c) * 16u - 1024u * uint32_t(q & 3);
     }
@@ -301,18 +306,21 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
   };
   auto group = [&](const Dest& d, int g) __attribute__((always_inline)) {
     dma16x4_biased(d.res, lb[4 * g] + d.add, lb[4 * g + 1] + d.add, lb[4 * g + 2] + d.add, lb[4 * g + 3] + d.add,
-                   lds_addr(d.slot) + uint32_t(wave * R::PW + 4 * g) * 1024u);
+                   lds_addr(d.slot) + uint32_t(q0 + 4 * g) * 1024u);
   };
   {
     const Dest d0 = dest(0);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) group(d0, g);
+    for (int g = 0; g < 4; ++g)
+      if (g < ngroups) group(d0, g);
   }
   if (ntiles > 1) {
     const Dest d1 = dest(1);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) group(d1, g);
-    wait_vm<R::PW>();   // own loads of stage 0
+    for (int g = 0; g < 4; ++g)
+      if (g < ngroups) group(d1, g);
+    if (wside) wait_vm<R::PWW>();   // own loads of stage 0
+    else wait_vm<R::PWX>();
   } else {
     wait_vm<0>();
   }
@@ -366,15 +374,13 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
       const char* nx = smem + ((s < 3 ? P : P + 1) & 1) * R::STAGE;
       auto rd = [&](int g) __attribute__((always_inline)) {
         fa[nb][g] = read_frag(nx, wrow + g * 32 + rl, 2 * ns + ch);
-        fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
+        if (g < C::FM) fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
       };
       auto chunk = [&](auto gc) __attribute__((always_inline)) {
         constexpr int g = decltype(gc)::value;
         if constexpr (s == 3 && g == 0) {
-          mfma(buf, 0, 0);
-          mfma(buf, 0, 1);
-          mfma(buf, 0, 2);
-          mfma(buf, 0, 3);
+#pragma unroll
+          for (int j = 0; j < C::FM; ++j) mfma(buf, 0, j);
           __builtin_amdgcn_sched_barrier(0);
           // own loads of stage t+1 landed; after the barrier every wave's
           // have, and every wave has read all of stage t
@@ -383,27 +389,31 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
           __builtin_amdgcn_sched_barrier(0);
           rd(0);
           next = dest(live ? t + 2 : t);
-          if (live) group(next, 0);
+          if (live) group(next, 0);   // every wave has at least two groups
           __builtin_amdgcn_sched_barrier(0);
           return;
         }
+        // the chunk's MFMAs (one row block against the wave's FM column
+        // blocks) with one fragment read of the next substep after each of
+        // the first two
+        constexpr bool XREAD = g < C::FM;
         mfma(buf, g, 0);
         fa[nb][g] = read_frag(nx, wrow + g * 32 + rl, 2 * ns + ch);
         mfma(buf, g, 1);
-        fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
-        mfma(buf, g, 2);
-        mfma(buf, g, 3);
+        if constexpr (XREAD) fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
+#pragma unroll
+        for (int j = 2; j < C::FM; ++j) mfma(buf, g, j);
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+        if constexpr (XREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if constexpr (C::FM > 2) __builtin_amdgcn_sched_group_barrier(0x008, C::FM - 2, 0);
         __builtin_amdgcn_sched_barrier(0);
         if constexpr (s == 3 && g == 1) {
           if (live) group(next, 1);
         }
         if constexpr (s == 0 && g >= 2) {
-          if (held_live) group(held, g);
+          if (held_live && g < ngroups) group(held, g);
         }
         __builtin_amdgcn_sched_barrier(0);
       };
@@ -662,11 +672,15 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
   }
 }
 
-// Tile choices.  Output: 256x256 tiles, four waves of 128 x 128, one per SIMD,
-// 256 fp32 accumulators per lane (in AGPRs), 128 KiB of LDS for the ring.
+// Tile choices.  Output: 256 weight rows by 256, 192 or 128 activation rows,
+// four waves of 128 x 128, 96 or 64, one per SIMD, up to 256 fp32 accumulators
+// per lane (in AGPRs), up to 128 KiB of LDS for the ring.  The host picks the
+// height per call (main_tile_rows).
 // Shrink: 128x128 tiles, so a 256-wide rank still gives two blocks per row
 // tile.  (Batches of at most 128 rows take the decode kernel.)
 using MainBig = Tile<256, 256, 2, 2>;
+using Main192 = Tile<256, 192, 2, 2>;
+using Main128 = Tile<256, 128, 2, 2>;
 using ShrinkBig = Tile<128, 128, 2, 2>;
 
 template <class C>
@@ -703,10 +717,41 @@ hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const Adapt
   return launch_shrink_t<ShrinkBig>(p, st, at, sp, stream);
 }
 
+int main_tile_rows(int M, int N) {
+  // Blocks run one per CU in whole waves of the chip, so a call takes about
+  // ceil(tiles / CUs) tile times.  A tile's time shrinks far less than its
+  // height, since the loop is bound per stage by its loads more than by its
+  // MFMAs: whole calls running a single wave of tiles took 1 : 0.90 : 0.83 for
+  // 256, 192 and 128 rows.  Take the height with the fewest tile times.
+  constexpr int kCUs = 256;
+  const int ntn = (N + 255) / 256;
+  int best = 256;
+  double best_cost = 0;
+  for (const int tm : {256, 192, 128}) {
+    const double tile_time = tm == 256 ? 1.0 : tm == 192 ? 0.90 : 0.83;
+    const int64_t tiles = int64_t(ntn) * ((M + tm - 1) / tm);
+    const double cost = double((tiles + kCUs - 1) / kCUs) * tile_time;
+    if (tm == 256 || cost < best_cost) {
+      best = tm;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
 hipError_t launch_bf16_main(const ProjArgs& p, const SegTable& st, const AdapterTable& at, bool has_adapter,
                             bool f32_out, hipStream_t stream, hipEvent_t e0, hipEvent_t e1) {
-  return f32_out ? launch_main_t<MainBig, true>(p, st, at, has_adapter, stream, e0, e1)
-                 : launch_main_t<MainBig, false>(p, st, at, has_adapter, stream, e0, e1);
+  switch (main_tile_rows(p.M, p.N)) {
+    case 128:
+      return f32_out ? launch_main_t<Main128, true>(p, st, at, has_adapter, stream, e0, e1)
+                     : launch_main_t<Main128, false>(p, st, at, has_adapter, stream, e0, e1);
+    case 192:
+      return f32_out ? launch_main_t<Main192, true>(p, st, at, has_adapter, stream, e0, e1)
+                     : launch_main_t<Main192, false>(p, st, at, has_adapter, stream, e0, e1);
+    default:
+      return f32_out ? launch_main_t<MainBig, true>(p, st, at, has_adapter, stream, e0, e1)
+                     : launch_main_t<MainBig, false>(p, st, at, has_adapter, stream, e0, e1);
+  }
 }
 
 }  // namespace lora

@@ -135,6 +135,10 @@ struct DecodePlan {
 DecodePlan decode_plan(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t trank, int64_t n_used);
 int decode_mtiles(int64_t M);
 
+// Activation rows per output tile of the prefill output kernel for an M x N
+// call (256, 192 or 128), chosen by whole waves of tiles over the CUs.
+int main_tile_rows(int M, int N);
+
 // Launchers (return the HIP status of the launch).
 hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const AdapterTable& at, const ShrinkPlan& sp,
                               hipStream_t stream);

@@ -85,6 +85,22 @@ def test_workspace_and_path_queries():
     assert bd.path(64, 512, 252, 16) == "invalid"
 
 
+def test_tile_rows_choice():
+    """The prefill output kernel's tile height: the fewest whole waves of tile times over 256 CUs."""
+    assert bd.tile_rows(16384, 5120, 5120) == 256      # 1,280 tiles of 256 rows: 5 full waves
+    assert bd.tile_rows(16384, 17408, 5120) == 256
+    assert bd.tile_rows(32768, 5120, 5120) == 256
+    assert bd.tile_rows(2054, 5120, 5120) == 192       # mixed batch: 180 tiles of 256 rows, 220 of 192
+    assert bd.tile_rows(2054, 17408, 5120) == 192
+    assert bd.tile_rows(700, 17408, 136) == 256        # 204 tiles; 192 or 128 rows would take two waves
+    assert bd.tile_rows(700, 11008, 136) == 192
+    assert bd.tile_rows(300, 1000, 136) == 128
+    assert bd.tile_rows(129, 5120, 5120) == 128
+    assert bd.tile_rows(128, 5120, 5120) == 0          # decode path
+    assert bd.tile_rows(300, 1000, 136, "f32") == 0    # test mode
+    assert bd.tile_rows(300, 1000, 252) == 0           # invalid K
+
+
 def call(**kw):
     a = dict(X=FAKE, seg_starts=[0, 32, 64], seg_adapter=[-1, 0], W=FAKE2, A=[FAKE3], B=[FAKE4], rank=16,
              scale=0.5, Y=FAKE5, M=64, N=512, K=256, dtype="bf16", workspace=FAKE * 320,
