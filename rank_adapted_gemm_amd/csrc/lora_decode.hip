@@ -475,48 +475,74 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs d, AdapterTable 
       const char* ws = smem + (i % G::NS) * G::STAGE;
       const char* xs = ws + TR * RB;
       const int lim = K == KIND_E ? (RANKED ? at.rank[d.slot_adapter[cc.slot]] : d.rank) : d.K, e0 = cc.st * UK;
+      // TAIL: zero the chunks at or past lim (a unit that reaches past it).
+      // 4-bit weight units come in two versions, so that those short of lim
+      // (every one when K is a multiple of 64) carry no test: as one version
+      // the test became selects on every fragment register.  The bf16 units
+      // keep one version with the test, which measured faster (a second
+      // version cost the grouped bf16 stack 6%).
       const bool tail = lim - e0 < UK;
+      auto multiply = [&](auto tail_c) __attribute__((always_inline)) {
+        constexpr int TAIL = decltype(tail_c)::value;   // 0: none, 1: always, 2: if tail
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int ch = 4 * j + (lane >> 4);
-        bf16x8 a[2], bx[MT];
-        if constexpr (Q4 && K == KIND_W) {
-          // 8 codes of row 16 rg + lane % 16 (of this wave's 32), k = 32 j + 8 (lane / 16) ..,
-          // dequantized with the row's group params: w = s (q - z), rounded to bf16
-          const char* wq = ws + wave * 4096;
+        for (int j = 0; j < 2; ++j) {
+          const int ch = 4 * j + (lane >> 4);
+          bf16x8 a[2], bx[MT];
+          if constexpr (Q4 && K == KIND_W) {
+            // 8 codes of row 16 rg + lane % 16 (of this wave's 32), k = 32 j + 8 (lane / 16) ..,
+            // dequantized with the row's group params: w = s (q - z), rounded to bf16
+            const char* wq = ws + wave * 4096;
 #pragma unroll
-          for (int rg = 0; rg < 2; ++rg) {
-            const int rr = rg * 16 + (lane & 15);
-            const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + rr * 32 + j * 16 + (lane >> 4) * 4);
-            const uint32_t prm = *reinterpret_cast<const uint32_t*>(wq + 1024 + rr * 4);
-            const float sc = __uint_as_float(prm << 16);
-            const float nsz = -sc * float((prm >> 16) & 0xFFu);     // -s z
-            // even codes in the bytes of lo, odd codes in the bytes of hi: one
-            // byte-to-float conversion and one fused multiply-add per code
-            const uint32_t lo = codes & 0x0F0F0F0Fu, hi = (codes >> 4) & 0x0F0F0F0Fu;
+            for (int rg = 0; rg < 2; ++rg) {
+              const int rr = rg * 16 + (lane & 15);
+              const uint32_t codes = *reinterpret_cast<const uint32_t*>(wq + rr * 32 + j * 16 + (lane >> 4) * 4);
+              const uint32_t prm = *reinterpret_cast<const uint32_t*>(wq + 1024 + rr * 4);
+              const float sc = __uint_as_float(prm << 16);
+              const float nsz = -sc * float((prm >> 16) & 0xFFu);     // -s z
+              // even codes in the bytes of lo, odd codes in the bytes of hi;
+              // code pair (2p, 2p+1) is byte p of each.  One byte-to-float
+              // conversion (v_cvt_f32_ubyteN reads byte N in place) and one
+              // fused multiply-add per code, one packed conversion per pair.
+              // The masks are opaque to the compiler, which would otherwise
+              // fold them into a shift and a mask per code.
+              uint32_t lo, hi;
+              asm("v_and_b32 %0, 0x0f0f0f0f, %1" : "=v"(lo) : "v"(codes));
+              asm("v_bfe_u32 %0, %1, 4, 28\n\tv_and_b32 %0, 0x0f0f0f0f, %0" : "=&v"(hi) : "v"(codes));
+              u32x4 w;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-              const uint32_t byte = ((e & 1) ? hi : lo) >> (8 * (e >> 1));
-              a[rg][e] = static_cast<__bf16>(__builtin_fmaf(sc, float(byte & 0xFFu), nsz));
+              for (int q = 0; q < 4; ++q) {
+                const float f0 = __builtin_fmaf(sc, float((lo >> (8 * q)) & 0xFFu), nsz);
+                const float f1 = __builtin_fmaf(sc, float((hi >> (8 * q)) & 0xFFu), nsz);
+                w[q] = __builtin_bit_cast(uint32_t, bf16x2{static_cast<__bf16>(f0), static_cast<__bf16>(f1)});
+              }
+              a[rg] = __builtin_bit_cast(bf16x8, w);
+            }
+          } else {
+#pragma unroll
+            for (int rg = 0; rg < 2; ++rg) a[rg] = frag(ws, wave * 32 + rg * 16 + (lane & 15), ch);
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) bx[mt] = frag(xs, mt * 16 + (lane & 15), ch);
+          if constexpr (TAIL != 0) {
+            if ((TAIL == 1 || tail) && e0 + ch * 8 >= lim) {
+#pragma unroll
+              for (int rg = 0; rg < 2; ++rg) a[rg] = bf16x8{};
+#pragma unroll
+              for (int mt = 0; mt < MT; ++mt) bx[mt] = bf16x8{};
             }
           }
-        } else {
 #pragma unroll
-          for (int rg = 0; rg < 2; ++rg) a[rg] = frag(ws, wave * 32 + rg * 16 + (lane & 15), ch);
+          for (int rg = 0; rg < 2; ++rg)
+#pragma unroll
+            for (int mt = 0; mt < MT; ++mt)
+              acc[rg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg], bx[mt], acc[rg][mt], 0, 0, 0);
         }
-#pragma unroll
-        for (int mt = 0; mt < MT; ++mt) bx[mt] = frag(xs, mt * 16 + (lane & 15), ch);
-        if (tail && e0 + ch * 8 >= lim) {
-#pragma unroll
-          for (int rg = 0; rg < 2; ++rg) a[rg] = bf16x8{};
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) bx[mt] = bf16x8{};
-        }
-#pragma unroll
-        for (int rg = 0; rg < 2; ++rg)
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt)
-            acc[rg][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[rg], bx[mt], acc[rg][mt], 0, 0, 0);
+      };
+      if constexpr (Q4 && K == KIND_W) {
+        if (tail) multiply(std::integral_constant<int, 1>{});
+        else multiply(std::integral_constant<int, 0>{});
+      } else {
+        multiply(std::integral_constant<int, 2>{});
       }
       if (deferred && i + 1 == n0) {   // the last W unit is multiplied: wait for T, issue the expand units
         deferred = false;
