@@ -311,7 +311,11 @@ size_t lora_proj_q4_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t ran
  * n_adapters adapters (an upper bound), counter area included.  Returns 0 for invalid
  * arguments.  Batches of at most 128 rows (the decode path) always need a workspace, for its
  * counters and split-K partial sums; larger batches need one only when some row names an
- * adapter. */
+ * adapter: the counter area, s X A^T (M x n_slices rank, 4 bytes an element) and, when the
+ * grid of 128 x 128 tiles of s X A^T is small (at most 128 tiles, ceil(M/128) x
+ * ceil(n_slices rank / 128)) and K long enough to give each split at least 8 steps of 64
+ * (K > 960), fp32 partial sums of that product split over K (64 KiB per tile and split, at
+ * most 8 splits). */
 size_t lora_proj_workspace_bytes(int64_t M, int64_t N, int64_t K, int32_t rank, int32_t n_adapters,
                                  lora_dtype dtype);
 

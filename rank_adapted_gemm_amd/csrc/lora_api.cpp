@@ -56,6 +56,7 @@ bool decode_counters_fit(int64_t N) { return ((N + 127) / 128 + 3) * 8 <= int64_
 lora::ShrinkPlan shrink_plan(const SegTable& st, int32_t n_adapters) {
   lora::ShrinkPlan sp{};
   sp.n_adapters = n_adapters;
+  sp.splits = 1;
   for (int g = 0; g < st.n; ++g)
     if (st.adapter[g] >= 0) sp.rows[st.adapter[g]] += st.start[g + 1] - st.start[g];
   sp.tile_off[0] = 0;
@@ -93,14 +94,54 @@ int64_t plan_rank(int64_t rank) { return rank_ok(rank) ? rank : 256; }
 // `slices` x rank wide.
 size_t r256(size_t x) { return (x + 255) & ~size_t(255); }
 
+// K splits of the bf16 shrink, from the shape alone (so calls that differ only
+// in how their adapters are stored sum in the same order): enough blocks to
+// cover the chip when the grid of 128 x 128 tiles, estimated as
+// ceil(M/128) x ceil(trank/128), is small; at most 8, each split at least 8
+// stages of 64, and the partials of up to LORA_MAX_ADAPTERS adapters' tiles
+// within 128 MiB.
+int shrink_splits(int64_t M, int64_t K, int64_t trank) {
+  const int64_t rt = lora::kShrinkRows;
+  const int64_t ntn = (trank + rt - 1) / rt, ntm = (M + rt - 1) / rt;
+  const int64_t tiles = std::max<int64_t>(1, ntn * ntm), nk = (K + 63) / 64;
+  int64_t s = std::min<int64_t>({8, 256 / tiles, nk / 8});
+  while (s > 1 && s * ntn * (ntm + LORA_MAX_ADAPTERS) * int64_t(lora::kShrinkPartBytes) > (int64_t(128) << 20)) --s;
+  return int(std::max<int64_t>(1, s));
+}
+
+// Bytes of the split shrink's partials: one per (tile, split), the tiles of
+// n_used adapters bounded by ceil(trank/128) x (ceil(M/128) + n_used).
+size_t part_bytes(int64_t M, int64_t K, int64_t trank, int64_t n_used) {
+  const int s = shrink_splits(M, K, trank);
+  if (s == 1 || n_used == 0) return 0;
+  const int64_t rt = lora::kShrinkRows;
+  return size_t(s) * size_t((trank + rt - 1) / rt) * size_t((M + rt - 1) / rt + n_used) * lora::kShrinkPartBytes;
+}
+
+// The prefill path's regions after the counters: T (when an adapter is
+// named), the bf16 copy of 4-bit weights, then the shrink's partials.
+struct PrefillLayout {
+  size_t off_w, off_part, part, total;
+};
+PrefillLayout prefill_layout(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t slices, int64_t n_used, bool q4) {
+  PrefillLayout l;
+  const size_t tb = n_used ? t_bytes(M, slices * rank) : 0;
+  l.off_w = LORA_WORKSPACE_COUNTER_BYTES + r256(tb);
+  const size_t end = q4 ? l.off_w + size_t(N) * size_t(K) * 2 : LORA_WORKSPACE_COUNTER_BYTES + tb;
+  l.part = part_bytes(M, K, slices * rank, n_used);
+  l.off_part = l.part ? r256(end) : end;
+  l.total = l.off_part + l.part;
+  return l;
+}
+
 // With 4-bit weights the prefill path also keeps a bf16 copy of W after T.
 size_t need_bytes(int64_t M, int64_t N, int64_t K, int64_t rank, int64_t slices, int64_t n_used, lora_dtype dtype,
                   bool q4 = false) {
   if (dtype != LORA_F32 && small_m(M))
     return lora::decode_plan(M, N, K, plan_rank(rank), slices * plan_rank(rank), n_used).total;
-  if (q4)
-    return LORA_WORKSPACE_COUNTER_BYTES + (n_used ? r256(t_bytes(M, slices * rank)) : 0) + size_t(N) * size_t(K) * 2;
-  return n_used ? LORA_WORKSPACE_COUNTER_BYTES + t_bytes(M, slices * rank) : 0;
+  if (!q4 && !n_used) return 0;
+  if (dtype == LORA_F32) return LORA_WORKSPACE_COUNTER_BYTES + t_bytes(M, slices * rank);
+  return prefill_layout(M, N, K, rank, slices, n_used, q4).total;
 }
 
 // Extra checks of a call with 4-bit weights: the bf16 kernels only, K a
@@ -388,14 +429,20 @@ lora_status run_call(const void* X, const int32_t* seg_starts, const int32_t* se
     if (has_adapter) e = lora::launch_f32_shrink(p, tbl, at, stream);
     if (e == hipSuccess) e = lora::launch_f32_main(p, tbl, at, has_adapter, stream, main_start, main_stop);
   } else {
+    const PrefillLayout lay = prefill_layout(M, N, K, rank, sl.n, n_used, q4);
     if (q4) {   // expand the 4-bit weights into a bf16 copy after T, then run the bf16 kernels
-      char* wcopy = static_cast<char*>(workspace) + LORA_WORKSPACE_COUNTER_BYTES +
-                    (has_adapter ? r256(t_bytes(M, int64_t(rank) * sl.n)) : 0);
+      char* wcopy = static_cast<char*>(workspace) + lay.off_w;
       e = lora::launch_q4_dequant(W, WP, wcopy, N, K, stream);
       p.W = wcopy;
       p.w_bytes = uint32_t(size_t(N) * size_t(K) * 2);
     }
-    if (e == hipSuccess && has_adapter) e = lora::launch_bf16_shrink(p, tbl, at, shrink_plan(tbl, n_adapters), stream);
+    if (e == hipSuccess && has_adapter) {
+      lora::ShrinkPlan sp = shrink_plan(tbl, n_adapters);
+      sp.splits = lay.part ? shrink_splits(M, K, p.trank) : 1;
+      sp.part = lay.part ? static_cast<char*>(workspace) + lay.off_part : nullptr;
+      sp.part_bytes = uint32_t(lay.part);
+      e = lora::launch_bf16_shrink(p, tbl, at, sp, stream);
+    }
     if (e == hipSuccess)
       e = lora::launch_bf16_main(p, tbl, at, has_adapter, dtype == LORA_BF16_F32OUT, stream, main_start, main_stop);
   }

@@ -475,27 +475,10 @@ __device__ __forceinline__ void tile_of_block(int b, int ntn, int ntm, int& tn, 
 // LDS row map, then stores T = s_a acc as bf16 hi and lo parts on those rows.
 // One K loop per tile whatever the batch's interleaving of adapters, and no
 // rows computed only to be dropped, except in each adapter's last tile.
+// Row of X behind each of a shrink tile's virtual rows: adapter a's segments
+// in row order, concatenated (-1 past its last row).
 template <class C>
-__global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, AdapterTable at, ShrinkPlan sp, int ntn,
-                                                       int ntm) {
-  static_assert(C::TM == kShrinkRows, "shrink tiles are planned in kShrinkRows rows");
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
-  __shared__ int phys[C::TM];
-  int tn, tv;
-  tile_of_block(blockIdx.x, ntn, ntm, tn, tv);
-  int a = 0;                                   // the adapter whose virtual rows tile tv covers
-  while (a + 1 < sp.n_adapters && sp.tile_off[a + 1] <= tv) ++a;
-  const int v0 = (tv - sp.tile_off[a]) * C::TM, nrows = min(C::TM, sp.rows[a] - v0);
-  const int j0 = tn * C::TN;
-  const int atrank = p.sl.n * at.rank[a];      // rows of A_a
-  if (j0 >= atrank) return;                    // a rank tile past this adapter's rank (whole block)
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % C::WN, wm = wave / C::WN;
-  const auto tres = make_rsrc(p.T, p.t_bytes);
-  const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.trank) * 2u;   // T_lo follows T_hi
-
-  // row of X behind each of the tile's virtual rows: adapter a's segments in
-  // row order, concatenated (-1 past its last row)
+__device__ __forceinline__ void shrink_rows(int* phys, const SegTable& st, int a, int v0, int nrows, int tid) {
   for (int r = tid; r < C::TM; r += C::NT) {
     int row = -1;
     if (r < nrows) {
@@ -512,21 +495,31 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
     }
     phys[r] = row;
   }
-  __syncthreads();
+}
 
-  const Side as{make_rsrc_words(at.A[a], at.a_bytes[a]), uint32_t(p.K) * 2u, j0, 0, atrank};
-  const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, 0, 0, 0};
-  f32x16 acc[C::FN][C::FM];
-#pragma unroll
-  for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
-  const int nk = (p.K + BK - 1) / BK;
-  k_loop<C, false, true>(acc, nk, p.K / BK, p.K,
-                         [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = t * BK; },
-                         smem, tid, wn, wm, phys);
-  // acc[i][j][r]: rank index j0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
-  //               virtual row wm*(TM/WM) + j*32 + lane%32 of the tile
+// Tile `lt` of the shrink grid: its rank tile (j0), adapter, and first
+// virtual row and row count.
+struct ShrinkTile {
+  int j0, a, v0, nrows;
+};
+template <class C>
+__device__ __forceinline__ ShrinkTile shrink_tile(int lt, int ntn, int ntm, const ShrinkPlan& sp) {
+  int tn, tv;
+  tile_of_block(lt, ntn, ntm, tn, tv);
+  int a = 0;                                   // the adapter whose virtual rows tile tv covers
+  while (a + 1 < sp.n_adapters && sp.tile_off[a + 1] <= tv) ++a;
+  const int v0 = (tv - sp.tile_off[a]) * C::TM;
+  return ShrinkTile{tn * C::TN, a, v0, min(C::TM, sp.rows[a] - v0)};
+}
+
+// T = s_a acc on the tile's rows, as bf16 hi and lo parts.
+// acc[i][j][r]: rank index j0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
+//               virtual row wm*(TM/WM) + j*32 + lane%32 of the tile
+template <class C>
+__device__ __forceinline__ void store_t(const f32x16 (&acc)[C::FN][C::FM], const ProjArgs& p, float scale, int j0,
+                                        const int* phys, int wn, int wm, int lane) {
+  const auto tres = make_rsrc(p.T, p.t_bytes);
+  const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.trank) * 2u;   // T_lo follows T_hi
 #pragma unroll
   for (int j = 0; j < C::FM; ++j) {
     const int row = phys[wm * (C::TM / C::WM) + j * 32 + (lane & 31)];
@@ -537,7 +530,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
         const int jr = j0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
         float h[4], l[4];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) split_hi_lo(at.scale[a] * acc[i][j][q * 4 + e], h[e], l[e]);
+        for (int e = 0; e < 4; ++e) split_hi_lo(scale * acc[i][j][q * 4 + e], h[e], l[e]);
         const uint32_t off = (row >= 0 && jr < p.trank) ? (uint32_t(row) * uint32_t(p.trank) + uint32_t(jr)) * 2u
                                                         : kMaskedOffset;
         const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};
@@ -547,6 +540,111 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
                                               off == kMaskedOffset ? kMaskedOffset : off + lo_base, 0, 0);
       }
   }
+}
+
+// A partial's layout: per wave, per (i, j) fragment, per quarter q, the 64
+// lanes' four floats, so each store and load is one 1 KiB line per wave.
+template <class C>
+__device__ __forceinline__ uint32_t part_off(int wave, int i, int j, int q, int lane) {
+  return uint32_t((((wave * C::FN + i) * C::FM + j) * 4 + q) * 1024 + lane * 16);
+}
+
+// ------------------------------------------------------------------ shrink
+// Adapter-sorted: the rows that name adapter a, gathered from all its segments
+// in row order, form a virtual row range (ShrinkPlan), and the grid has one
+// block per (rank tile, virtual row tile).  A block computes
+// acc = A_a[rank tile] X[its rows]^T with the activation rows loaded through an
+// LDS row map, then stores T = s_a acc as bf16 hi and lo parts on those rows.
+// One K loop per tile whatever the batch's interleaving of adapters, and no
+// rows computed only to be dropped, except in each adapter's last tile.
+//
+// A grid of few tiles (a batch of few adapter rows) runs sp.splits blocks per
+// tile, each over its share of K, which store their fp32 partials; the sum in
+// split order (shrink_reduce_kernel) stores T, so the result does not depend
+// on timing.
+template <class C>
+__global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, AdapterTable at, ShrinkPlan sp, int ntn,
+                                                       int ntm) {
+  static_assert(C::TM == kShrinkRows && C::TN == kShrinkRows, "shrink tiles are planned in kShrinkRows rows");
+  static_assert(C::NW * C::FN * C::FM * 4 * 1024 == int(kShrinkPartBytes), "partial layout");
+  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
+  __shared__ int phys[C::TM];
+  const int ntiles = ntn * ntm;
+  const int lt = int(blockIdx.x) % ntiles, split = int(blockIdx.x) / ntiles;
+  const ShrinkTile tl = shrink_tile<C>(lt, ntn, ntm, sp);
+  const int atrank = p.sl.n * at.rank[tl.a];   // rows of A_a
+  if (tl.j0 >= atrank) return;                 // a rank tile past this adapter's rank (whole block)
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  shrink_rows<C>(phys, st, tl.a, tl.v0, tl.nrows, tid);
+  __syncthreads();
+
+  const Side as{make_rsrc_words(at.A[tl.a], at.a_bytes[tl.a]), uint32_t(p.K) * 2u, tl.j0, 0, atrank};
+  const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, 0, 0, 0};
+  f32x16 acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+  // this block's stages [t0, t1) of the nk; the K tail can only fall in the last
+  const int nk = (p.K + BK - 1) / BK;
+  const int t0 = split * nk / sp.splits, t1 = (split + 1) * nk / sp.splits;
+  const int nfull = p.K / BK;
+  k_loop<C, false, true>(acc, t1 - t0, max(0, min(t1, nfull) - t0), p.K,
+                         [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = (t0 + t) * BK; },
+                         smem, tid, wn, wm, phys);
+  if (sp.splits == 1) {
+    store_t<C>(acc, p, at.scale[tl.a], tl.j0, phys, wn, wm, lane);
+    return;
+  }
+  const auto pres = make_rsrc(sp.part, sp.part_bytes);
+  const uint32_t base = uint32_t(lt * sp.splits + split) * kShrinkPartBytes;
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const u32x4 w{__float_as_uint(acc[i][j][q * 4 + 0]), __float_as_uint(acc[i][j][q * 4 + 1]),
+                      __float_as_uint(acc[i][j][q * 4 + 2]), __float_as_uint(acc[i][j][q * 4 + 3])};
+        __builtin_amdgcn_raw_buffer_store_b128(w, pres, base + part_off<C>(wave, i, j, q, lane), 0, 0);
+      }
+}
+
+// T of the split shrink's tiles: each tile's partials summed in split order,
+// then stored as the unsplit shrink stores them.
+template <class C>
+__global__ __launch_bounds__(C::NT) void shrink_reduce_kernel(ProjArgs p, SegTable st, AdapterTable at, ShrinkPlan sp,
+                                                              int ntn, int ntm) {
+  __shared__ int phys[C::TM];
+  const int lt = int(blockIdx.x);
+  const ShrinkTile tl = shrink_tile<C>(lt, ntn, ntm, sp);
+  if (tl.j0 >= p.sl.n * at.rank[tl.a]) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % C::WN, wm = wave / C::WN;
+  shrink_rows<C>(phys, st, tl.a, tl.v0, tl.nrows, tid);
+  __syncthreads();
+  const auto pres = make_rsrc(sp.part, sp.part_bytes);
+  f32x16 acc[C::FN][C::FM];
+#pragma unroll
+  for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
+  for (int sp_i = 0; sp_i < sp.splits; ++sp_i) {
+    const uint32_t base = uint32_t(lt * sp.splits + sp_i) * kShrinkPartBytes;
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const f32x4 v = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, base + part_off<C>(wave, i, j, q, lane), 0, 0));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc[i][j][q * 4 + e] += v[e];
+        }
+  }
+  store_t<C>(acc, p, at.scale[tl.a], tl.j0, phys, wn, wm, lane);
 }
 
 // ------------------------------------------------------------------ main
@@ -694,7 +792,12 @@ hipError_t launch_shrink_t(const ProjArgs& p, const SegTable& st, const AdapterT
   ShrinkPlan spa = sp;
   int a0 = ntn, a1 = ntm;
   void* args[] = {&pa, &sa, &aa, &spa, &a0, &a1};
-  return hipLaunchKernel(reinterpret_cast<const void*>(&shrink_kernel<C>), dim3(ntn * ntm), dim3(C::NT), args, 0, s);
+  hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&shrink_kernel<C>), dim3(ntn * ntm * sp.splits),
+                                 dim3(C::NT), args, 0, s);
+  if (e == hipSuccess && sp.splits > 1)
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&shrink_reduce_kernel<C>), dim3(ntn * ntm), dim3(C::NT), args,
+                        0, s);
+  return e;
 }
 
 template <class C, bool F32_OUT>

@@ -29,7 +29,14 @@ struct ShrinkPlan {
   int32_t n_adapters;
   int32_t rows[LORA_MAX_ADAPTERS];
   int32_t tile_off[LORA_MAX_ADAPTERS + 1];
+  // K split: `splits` blocks per tile, each over its share of the 64-wide
+  // stages, store fp32 partials (kShrinkPartBytes per tile and split) at
+  // `part`; a second kernel sums them in split order.  1: no split.
+  int32_t splits;
+  void* part;
+  uint32_t part_bytes;
 };
+constexpr uint32_t kShrinkPartBytes = kShrinkRows * kShrinkRows * 4;
 
 // Adapter a has its own rank r_a (at most the call's rank r, the largest of
 // them): A_a is (S r_a) x K and B_a is N x r_a, and its rows of T hold S r_a

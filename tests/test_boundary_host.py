@@ -63,6 +63,13 @@ def test_workspace_and_path_queries():
     C = bd.WORKSPACE_COUNTER_BYTES
     assert bd.workspace_bytes(16384, 5120, 5120, 256) == C + 16384 * 256 * 4   # prefill: counters + s X A^T
     assert bd.workspace_bytes(16384, 5120, 5120, 256, 0) == 0                  # prefill, base only
+    # a small shrink grid (2054 rows: 17 x 2 tiles of 128) splits K = 5120 in 7 (256 // 34), with
+    # 64 KiB of fp32 partials per (tile, split) after T, the tiles bounded by 2 x (17 + 1 adapter)
+    r256 = lambda x: (x + 255) // 256 * 256  # noqa: E731
+    assert bd.workspace_bytes(2054, 5120, 5120, 256) == r256(C + 2054 * 256 * 4) + 7 * 2 * 18 * 65536
+    assert bd.workspace_bytes(2054, 5120, 17408, 256, 2) == r256(C + 2054 * 256 * 4) + 7 * 2 * 19 * 65536
+    assert bd.workspace_bytes(2054, 5120, 448, 256) == C + 2054 * 256 * 4     # 7 stages of K: no split
+    assert bd.workspace_bytes(2054, 5120, 5120, 256, 1, "f32") == C + 2054 * 256 * 4
     assert bd.workspace_bytes(70, 17408, 5120, 256, dtype="f32") == C + 70 * 256 * 4
     assert bd.workspace_bytes(64, 512, 250, 16) == 0          # K not a multiple of 8
     assert bd.workspace_bytes(64, 512, 256, 24) == 0          # rank not a multiple of 16

@@ -1,0 +1,110 @@
+"""Parity of the prefill shrink split over K, through the C-ABI.
+
+When the grid of 128 x 128 tiles of s X A^T is small and K long, the shrink runs several blocks
+per tile, each over its share of K's 64-wide steps; they store fp32 partials and a second kernel
+sums them in split order before T is stored.  Each case below splits (the count follows from the
+shape alone): 4 splits of 33 steps with the K tail in the last, 8 uneven splits of 65 steps, two
+rank tiles of which a rank-16 adapter's second is skipped, and a sliced call.  Adapters of short
+interleaved segments and base rows throughout.  Integer inputs: the fp32 store equals the exact
+result bit for bit and the bf16 store is its correct rounding.  Gaussian inputs: the G2 bar
+against the oracle, and the same bits on a second call."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+import gates
+from gpu_util import log, record, to_device, y_bits, y_to_numpy
+from oracle import lora_proj_ref, lora_proj_sliced_ref
+from rank_adapted_gemm_amd import binding as bd
+from rank_adapted_gemm_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+# shape, adapter ranks (one entry: every adapter at that rank), slice widths, and the splits the
+# shape gets: min(8, 256 // (ceil(M/128) ceil(trank/128)), ceil(K/64) // 8)
+CASES = {
+    "k2056": (dict(M=300, N=520, K=2056), [48], None, 4),
+    "k4104": (dict(M=300, N=264, K=4104), [32], None, 8),
+    "ranked": (dict(M=300, N=520, K=2056), [16, 256, 48], None, 4),
+    "sliced": (dict(M=400, N=None, K=1536), [32], [256, 512, 256], 3),
+}
+
+
+def table(seed, M):
+    """Segments of 1..60 rows naming one of three adapters or none."""
+    g = np.random.Generator(np.random.PCG64(seed))
+    starts, labels = [0], []
+    while starts[-1] < M:
+        starts.append(min(M, starts[-1] + int(g.integers(1, 61))))
+        labels.append(int(g.integers(-1, 3)))
+    return starts, labels
+
+
+def splits(M, K, trank):
+    ntn, ntm = -(-trank // 128), -(-M // 128)
+    return max(1, min(8, 256 // (ntn * ntm), -(-K // 64) // 8))
+
+
+def problem(name, seed, integer):
+    shape, ranks, slices, _ = CASES[name]
+    c = dict(shape)
+    if slices is not None:
+        c["N"] = sum(slices)
+    starts, labels = table(seed, c["M"])
+    p = synth.random_problem(seed, scale=[1.0, 0.5, -2.0] if integer else [0.7, 1.3, -0.4], integer=integer,
+                             rank=ranks[0], ranks=ranks if len(ranks) > 1 else ranks * 3, seg_starts=starts,
+                             seg_adapter=labels, n_adapters=3, slices=1 if slices is None else len(slices), **c)
+    return p, ranks, slices
+
+
+def oracle(p, slices):
+    if slices is None:
+        return lora_proj_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale)
+    return lora_proj_sliced_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, slices)
+
+
+def call(p, ranks, slices, dtype):
+    import torch
+    X, W, A, B = to_device(p)
+    if len(ranks) > 1:
+        y = bd.lora_proj_ranked(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, dtype=dtype,
+                                slices=slices)
+    else:
+        y = bd.lora_proj(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, dtype=dtype,
+                         slices=slices)
+    torch.cuda.synchronize()
+    return y
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_split_shrink_exact(name):
+    p, ranks, slices = problem(name, 71, integer=True)
+    trank = max(ranks) * (1 if slices is None else len(slices))
+    assert splits(p.M, p.K, trank) == CASES[name][3] > 1
+    assert bd.path(p.M, p.N, p.K, max(ranks)) == "prefill"
+    log(f"case split shrink exact {name} M={p.M} N={p.N} K={p.K} ranks={ranks} splits={CASES[name][3]}")
+    exact = oracle(p, slices)
+    assert np.all(np.abs(exact) < 2 ** 24)
+    y32 = y_to_numpy(call(p, ranks, slices, "bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(call(p, ranks, slices, "bf16")), gates.bf16_rne_of_f64(exact))
+
+
+@pytest.mark.parametrize("name", list(CASES))
+def test_split_shrink_gaussian(name):
+    p, ranks, slices = problem(name, 72, integer=False)
+    log(f"case split shrink gaussian {name} M={p.M} N={p.N} K={p.K}")
+    ref = oracle(p, slices)
+    y = call(p, ranks, slices, "bf16")
+    yn = y_to_numpy(y)
+    rep = gates.report(yn, ref)
+    over = np.abs(yn - ref) > gates.BF16_TOL * rep["rms"]
+    log(f"  split/{name} rms={rep['rms']:.4g} G1={rep['g1']:.3e} G2={rep['g2']:.3e} past-G1={int(over.sum())}")
+    record(f"split/{name}", rep, int(over.sum()))
+    assert rep["nonfinite"] == 0 and rep["g2"] <= gates.BF16_TOL, rep
+    if over.any():
+        assert gates.explained_by_rounding(yn[over], ref[over], rep["rms"]).all()
+    # the partials are summed in a fixed order: a second call gives the same bits
+    assert np.array_equal(y_bits(y), y_bits(call(p, ranks, slices, "bf16")))
