@@ -104,7 +104,7 @@ int shrink_splits(int64_t M, int64_t K, int64_t trank) {
   const int64_t rt = lora::kShrinkRows;
   const int64_t ntn = (trank + rt - 1) / rt, ntm = (M + rt - 1) / rt;
   const int64_t tiles = std::max<int64_t>(1, ntn * ntm), nk = (K + 63) / 64;
-  int64_t s = std::min<int64_t>({8, 256 / tiles, nk / 8});
+  int64_t s = std::min<int64_t>({lora::kShrinkMaxSplits, 256 / tiles, nk / 8});
   while (s > 1 && s * ntn * (ntm + LORA_MAX_ADAPTERS) * int64_t(lora::kShrinkPartBytes) > (int64_t(128) << 20)) --s;
   return int(std::max<int64_t>(1, s));
 }

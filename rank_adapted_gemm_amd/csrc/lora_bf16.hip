@@ -467,34 +467,22 @@ __device__ __forceinline__ void tile_of_block(int b, int ntn, int ntm, int& tn, 
   tn = in / gsz;
 }
 
-// ------------------------------------------------------------------ shrink
-// Adapter-sorted: the rows that name adapter a, gathered from all its segments
-// in row order, form a virtual row range (ShrinkPlan), and the grid has one
-// block per (rank tile, virtual row tile).  A block computes
-// acc = A_a[rank tile] X[its rows]^T with the activation rows loaded through an
-// LDS row map, then stores T = s_a acc as bf16 hi and lo parts on those rows.
-// One K loop per tile whatever the batch's interleaving of adapters, and no
-// rows computed only to be dropped, except in each adapter's last tile.
-// Row of X behind each of a shrink tile's virtual rows: adapter a's segments
-// in row order, concatenated (-1 past its last row).
+// Row of X behind virtual row v of adapter a: a's segments in row order,
+// concatenated (-1 past its last row).
+__device__ __forceinline__ int virtual_row(const SegTable& st, int a, int v) {
+  for (int g = 0; g < st.n; ++g) {
+    if (st.adapter[g] != a) continue;
+    const int len = st.start[g + 1] - st.start[g];
+    if (v < len) return st.start[g] + v;
+    v -= len;
+  }
+  return -1;
+}
+
+// The rows of X behind a shrink tile's virtual rows v0 .. v0 + nrows - 1.
 template <class C>
 __device__ __forceinline__ void shrink_rows(int* phys, const SegTable& st, int a, int v0, int nrows, int tid) {
-  for (int r = tid; r < C::TM; r += C::NT) {
-    int row = -1;
-    if (r < nrows) {
-      int v = v0 + r;
-      for (int g = 0; g < st.n; ++g) {
-        if (st.adapter[g] != a) continue;
-        const int len = st.start[g + 1] - st.start[g];
-        if (v < len) {
-          row = st.start[g] + v;
-          break;
-        }
-        v -= len;
-      }
-    }
-    phys[r] = row;
-  }
+  for (int r = tid; r < C::TM; r += C::NT) phys[r] = r < nrows ? virtual_row(st, a, v0 + r) : -1;
 }
 
 // Tile `lt` of the shrink grid: its rank tile (j0), adapter, and first
@@ -512,33 +500,40 @@ __device__ __forceinline__ ShrinkTile shrink_tile(int lt, int ntn, int ntm, cons
   return ShrinkTile{tn * C::TN, a, v0, min(C::TM, sp.rows[a] - v0)};
 }
 
-// T = s_a acc on the tile's rows, as bf16 hi and lo parts.
+// T = s_a acc of one 32 x 32 MFMA tile, as bf16 hi and lo parts:
+// acc[r] is rank index jt + (r/4)*8 + (lane/32)*4 + r%4 on the lane's row of X
+// (`row`, -1 for none).
+__device__ __forceinline__ void store_t_frag(const f32x16& acc, const ProjArgs& p, float scale, int jt, int row,
+                                             int lane) {
+  const auto tres = make_rsrc(p.T, p.t_bytes);
+  const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.trank) * 2u;   // T_lo follows T_hi
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int jr = jt + q * 8 + (lane >> 5) * 4;
+    float h[4], l[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) split_hi_lo(scale * acc[q * 4 + e], h[e], l[e]);
+    const uint32_t off = (row >= 0 && jr < p.trank) ? (uint32_t(row) * uint32_t(p.trank) + uint32_t(jr)) * 2u
+                                                    : kMaskedOffset;
+    const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};
+    const u32x2 lv{pack2(l[0], l[1]), pack2(l[2], l[3])};
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), tres, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, lv), tres,
+                                          off == kMaskedOffset ? kMaskedOffset : off + lo_base, 0, 0);
+  }
+}
+
+// T = s_a acc on the tile's rows.
 // acc[i][j][r]: rank index j0 + wn*(TN/WN) + i*32 + (r/4)*8 + (lane/32)*4 + r%4,
 //               virtual row wm*(TM/WM) + j*32 + lane%32 of the tile
 template <class C>
 __device__ __forceinline__ void store_t(const f32x16 (&acc)[C::FN][C::FM], const ProjArgs& p, float scale, int j0,
                                         const int* phys, int wn, int wm, int lane) {
-  const auto tres = make_rsrc(p.T, p.t_bytes);
-  const uint32_t lo_base = uint32_t(p.M) * uint32_t(p.trank) * 2u;   // T_lo follows T_hi
 #pragma unroll
   for (int j = 0; j < C::FM; ++j) {
     const int row = phys[wm * (C::TM / C::WM) + j * 32 + (lane & 31)];
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int jr = j0 + wn * (C::TN / C::WN) + i * 32 + q * 8 + (lane >> 5) * 4;
-        float h[4], l[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) split_hi_lo(scale * acc[i][j][q * 4 + e], h[e], l[e]);
-        const uint32_t off = (row >= 0 && jr < p.trank) ? (uint32_t(row) * uint32_t(p.trank) + uint32_t(jr)) * 2u
-                                                        : kMaskedOffset;
-        const u32x2 hv{pack2(h[0], h[1]), pack2(h[2], h[3])};
-        const u32x2 lv{pack2(l[0], l[1]), pack2(l[2], l[3])};
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, hv), tres, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, lv), tres,
-                                              off == kMaskedOffset ? kMaskedOffset : off + lo_base, 0, 0);
-      }
+    for (int i = 0; i < C::FN; ++i) store_t_frag(acc[i][j], p, scale, j0 + wn * (C::TN / C::WN) + i * 32, row, lane);
   }
 }
 
@@ -612,39 +607,43 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
 }
 
 // T of the split shrink's tiles: each tile's partials summed in split order,
-// then stored as the unsplit shrink stores them.
+// then stored as the unsplit shrink stores them.  One 32 x 32 MFMA tile per
+// wave: block b covers the part that wave b % NW of tile b / NW computed, its
+// wave w the fragment (w / FM, w % FM), with every split's loads in flight at
+// once.
 template <class C>
 __global__ __launch_bounds__(C::NT) void shrink_reduce_kernel(ProjArgs p, SegTable st, AdapterTable at, ShrinkPlan sp,
                                                               int ntn, int ntm) {
-  __shared__ int phys[C::TM];
-  const int lt = int(blockIdx.x);
+  static_assert(C::FN * C::FM == C::NW, "one fragment per wave");
+  const int lt = int(blockIdx.x) / C::NW, part = int(blockIdx.x) % C::NW;
   const ShrinkTile tl = shrink_tile<C>(lt, ntn, ntm, sp);
   if (tl.j0 >= p.sl.n * at.rank[tl.a]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % C::WN, wm = wave / C::WN;
-  shrink_rows<C>(phys, st, tl.a, tl.v0, tl.nrows, tid);
-  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int i = wave / C::FM, j = wave % C::FM;
+  const int wn = part % C::WN, wm = part / C::WN;
+  const int r = wm * (C::TM / C::WM) + j * 32 + (lane & 31);   // the lane's virtual row in the tile
+  const int row = r < tl.nrows ? virtual_row(st, tl.a, tl.v0 + r) : -1;
   const auto pres = make_rsrc(sp.part, sp.part_bytes);
-  f32x16 acc[C::FN][C::FM];
+  f32x4 v[kShrinkMaxSplits][4];
 #pragma unroll
-  for (int i = 0; i < C::FN; ++i)
+  for (int s_i = 0; s_i < kShrinkMaxSplits; ++s_i)
+    if (s_i < sp.splits) {
 #pragma unroll
-    for (int j = 0; j < C::FM; ++j) acc[i][j] = f32x16{};
-  for (int sp_i = 0; sp_i < sp.splits; ++sp_i) {
-    const uint32_t base = uint32_t(lt * sp.splits + sp_i) * kShrinkPartBytes;
+      for (int q = 0; q < 4; ++q)
+        v[s_i][q] = __builtin_bit_cast(
+            f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                       pres, uint32_t(lt * sp.splits + s_i) * kShrinkPartBytes + part_off<C>(part, i, j, q, lane), 0, 0));
+    }
+  f32x16 acc{};
 #pragma unroll
-    for (int i = 0; i < C::FN; ++i)
+  for (int s_i = 0; s_i < kShrinkMaxSplits; ++s_i)
+    if (s_i < sp.splits) {
 #pragma unroll
-      for (int j = 0; j < C::FM; ++j)
+      for (int q = 0; q < 4; ++q)
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const f32x4 v = __builtin_bit_cast(
-              f32x4, __builtin_amdgcn_raw_buffer_load_b128(pres, base + part_off<C>(wave, i, j, q, lane), 0, 0));
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc[i][j][q * 4 + e] += v[e];
-        }
-  }
-  store_t<C>(acc, p, at.scale[tl.a], tl.j0, phys, wn, wm, lane);
+        for (int e = 0; e < 4; ++e) acc[q * 4 + e] += v[s_i][q][e];
+    }
+  store_t_frag(acc, p, at.scale[tl.a], tl.j0 + wn * (C::TN / C::WN) + i * 32, row, lane);
 }
 
 // ------------------------------------------------------------------ main
@@ -795,8 +794,8 @@ hipError_t launch_shrink_t(const ProjArgs& p, const SegTable& st, const AdapterT
   hipError_t e = hipLaunchKernel(reinterpret_cast<const void*>(&shrink_kernel<C>), dim3(ntn * ntm * sp.splits),
                                  dim3(C::NT), args, 0, s);
   if (e == hipSuccess && sp.splits > 1)
-    e = hipLaunchKernel(reinterpret_cast<const void*>(&shrink_reduce_kernel<C>), dim3(ntn * ntm), dim3(C::NT), args,
-                        0, s);
+    e = hipLaunchKernel(reinterpret_cast<const void*>(&shrink_reduce_kernel<C>), dim3(ntn * ntm * C::NW), dim3(C::NT),
+                        args, 0, s);
   return e;
 }
 

@@ -37,6 +37,7 @@ struct ShrinkPlan {
   uint32_t part_bytes;
 };
 constexpr uint32_t kShrinkPartBytes = kShrinkRows * kShrinkRows * 4;
+constexpr int kShrinkMaxSplits = 8;
 
 // Adapter a has its own rank r_a (at most the call's rank r, the largest of
 // them): A_a is (S r_a) x K and B_a is N x r_a, and its rows of T hold S r_a
