@@ -4,8 +4,9 @@ When the grid of 128 x 128 tiles of s X A^T is small and K long, the shrink runs
 per tile, each over its share of K's 64-wide steps; they store fp32 partials and a second kernel
 sums them in split order before T is stored.  Each case below splits (the count follows from the
 shape alone): 4 splits of 33 steps with the K tail in the last, 8 uneven splits of 65 steps, two
-rank tiles of which a rank-16 adapter's second is skipped, and a sliced call.  Adapters of short
-interleaved segments and base rows throughout.  Integer inputs: the fp32 store equals the exact
+rank tiles of which a rank-16 adapter's second is skipped, a sliced call, and 32 adapters of a few
+rows each (32 row tiles where ceil(M/128) is 3: the partials' bound of ceil(M/128) + n_used row
+tiles).  Adapters of short interleaved segments and base rows throughout.  Integer inputs: the fp32 store equals the exact
 result bit for bit and the bf16 store is its correct rounding.  Gaussian inputs: the G2 bar
 against the oracle, and the same bits on a second call."""
 from __future__ import annotations
@@ -21,23 +22,29 @@ from rank_adapted_gemm_amd import synth
 
 pytestmark = pytest.mark.gpu
 
-# shape, adapter ranks (one entry: every adapter at that rank), slice widths, and the splits the
-# shape gets: min(8, 256 // (ceil(M/128) ceil(trank/128)), ceil(K/64) // 8)
+# shape, adapter ranks (one entry: every adapter at that rank), slice widths, the splits the
+# shape gets (min(8, 256 // (ceil(M/128) ceil(trank/128)), ceil(K/64) // 8)), and the adapters
 CASES = {
-    "k2056": (dict(M=300, N=520, K=2056), [48], None, 4),
-    "k4104": (dict(M=300, N=264, K=4104), [32], None, 8),
-    "ranked": (dict(M=300, N=520, K=2056), [16, 256, 48], None, 4),
-    "sliced": (dict(M=400, N=None, K=1536), [32], [256, 512, 256], 3),
+    "k2056": (dict(M=300, N=520, K=2056), [48], None, 4, 3),
+    "k4104": (dict(M=300, N=264, K=4104), [32], None, 8, 3),
+    "ranked": (dict(M=300, N=520, K=2056), [16, 256, 48], None, 4, 3),
+    "sliced": (dict(M=400, N=None, K=1536), [32], [256, 512, 256], 3, 3),
+    "many": (dict(M=300, N=264, K=4104), [16], None, 8, 32),
 }
 
 
-def table(seed, M):
-    """Segments of 1..60 rows naming one of three adapters or none."""
+def table(seed, M, n_adapters):
+    """Segments of 1..60 rows naming one of the adapters or none; with many adapters, segments of
+    1..9 rows naming each adapter in turn (every eighth none)."""
     g = np.random.Generator(np.random.PCG64(seed))
     starts, labels = [0], []
     while starts[-1] < M:
-        starts.append(min(M, starts[-1] + int(g.integers(1, 61))))
-        labels.append(int(g.integers(-1, 3)))
+        if n_adapters <= 3:
+            starts.append(min(M, starts[-1] + int(g.integers(1, 61))))
+            labels.append(int(g.integers(-1, n_adapters)))
+        else:
+            starts.append(min(M, starts[-1] + int(g.integers(1, 10))))
+            labels.append(-1 if len(labels) % 8 == 7 else (len(labels) - len(labels) // 8) % n_adapters)
     return starts, labels
 
 
@@ -47,14 +54,16 @@ def splits(M, K, trank):
 
 
 def problem(name, seed, integer):
-    shape, ranks, slices, _ = CASES[name]
+    shape, ranks, slices, _, n_adapters = CASES[name]
     c = dict(shape)
     if slices is not None:
         c["N"] = sum(slices)
-    starts, labels = table(seed, c["M"])
-    p = synth.random_problem(seed, scale=[1.0, 0.5, -2.0] if integer else [0.7, 1.3, -0.4], integer=integer,
-                             rank=ranks[0], ranks=ranks if len(ranks) > 1 else ranks * 3, seg_starts=starts,
-                             seg_adapter=labels, n_adapters=3, slices=1 if slices is None else len(slices), **c)
+    starts, labels = table(seed, c["M"], n_adapters)
+    scales = [1.0, 0.5, -2.0] if integer else [0.7, 1.3, -0.4]
+    p = synth.random_problem(seed, scale=[scales[a % 3] for a in range(n_adapters)], integer=integer,
+                             rank=ranks[0], ranks=ranks if len(ranks) > 1 else ranks * n_adapters,
+                             seg_starts=starts, seg_adapter=labels, n_adapters=n_adapters,
+                             slices=1 if slices is None else len(slices), **c)
     return p, ranks, slices
 
 
