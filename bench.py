@@ -56,11 +56,18 @@ def log(msg):
 
 # ------------------------------------------------------------------ HIP events
 class HipEvents:
-    """hipEvent_t pairs through the HIP runtime (the output kernel is timed on its own stream)."""
+    """hipEvent_t pairs through the HIP runtime (the output kernel is timed on its own stream).
+
+    The events only time: they are created without the system-scope fence (a cache writeback and
+    invalidate) that a default event performs when it is recorded.  Each record still leaves the
+    GPU idle for a few microseconds before the next launch.  The step's wall clock ends with a
+    full device synchronization."""
+
+    DISABLE_SYSTEM_FENCE = 0x20000000   # hipEventDisableSystemFence
 
     def __init__(self):
         self.lib = bd.load()      # resolves to the process's one HIP runtime (torch's)
-        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
         self.events = []
@@ -68,8 +75,8 @@ class HipEvents:
     def pair(self):
         a, b = ctypes.c_void_p(), ctypes.c_void_p()
         for e in (a, b):
-            if self.lib.hipEventCreate(ctypes.byref(e)) != 0:
-                raise RuntimeError("hipEventCreate failed")
+            if self.lib.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
             self.events.append(e)
         return a.value, b.value
 
@@ -189,9 +196,8 @@ class StepRunner:
 def time_steps(runner, steps, warmup, hip, events=True):
     """Wall time of `steps` steps; with `events`, also each output kernel's duration.
 
-    Event records cost a few microseconds of idle GPU time around each launch:
-    negligible next to a prefill kernel, but not next to a ~10 us decode call,
-    so the decode stack is timed without them.
+    The decode stack is timed without events: a record costs a little time even without
+    its system fence, which matters next to a ~10 us decode call.
     """
     import torch
     for _ in range(warmup):
