@@ -239,25 +239,31 @@ __device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, 
 // 128 x 64.  The ring holds two 64 KiB stages of BK = 64.
 //
 // A stage is four substeps of 16 MFMAs, each with the next substep's 8
-// fragment reads among its MFMAs.  A wave's 16 loads of a stage go out in
-// four groups of four (one M0 each):
+// fragment reads among its MFMAs, and one barrier, after the first 4 MFMAs of
+// substep 3 (stage t+1 is in its slot; no wave still reads stage t's).
 //
-//   substep 3 of stage t:    4 MFMAs, then the barrier (stage t+1 landed, no
-//                            wave still reads stage t's slot); groups 0 and 1
-//                            of stage t+2 into that slot
-//   substep 0 of stage t+1:  groups 2 and 3, after its 12th and 16th MFMA
-//
-// Spreading them so (rather than all 16 right after the barrier) keeps the
-// texture path from backing up into the MFMA stream, and the MFMAs issued
-// before the barrier cover a little of the waves' skew there.
+// Loads go through registers.  Waves 0 and 1 load the weight rows, waves 2
+// and 3 the activation rows: 16 (or, on the activation side of a shorter
+// tile, 12 or 8) 16-byte loads per lane and stage, each one 8-row group of
+// whole 128-byte lines.  Each load has a fixed chunk of the stage (four MFMAs),
+// where the wave writes the register into the free ring slot (ds_write_b128)
+// and loads it again, one stage ahead.  Chunks before the barrier write stage
+// t+1 into the other slot and load stage t+2; the three after it write stage
+// t+2 into stage t's slot and load stage t+3.  Every load has one stage to land,
+// no load waits on a slot, and the loads spread evenly over the MFMA stream.
 template <class C>
 struct WideRing {
   static constexpr int STAGE = C::STAGE;        // 64 KiB for 256 x 256
-  // 8-row loads per stage of each weight-side wave (waves 0, 1) and each
-  // activation-side wave (waves 2, 3): four groups of four, or fewer on the
-  // activation side of a shorter tile
-  static constexpr int PWW = C::TN / 16, PWX = C::TM / 16;
-  static_assert(C::NW == 4 && PWW == 16 && PWX % 4 == 0 && PWX >= 8 && PWX <= 16, "load groups of four");
+  static constexpr int PWW = C::TN / 16, PWX = C::TM / 16;   // loads per lane and stage
+  static_assert(C::NW == 4 && PWW == 16 && PWX >= 8 && PWX <= 16, "one load per chunk at most");
+  // chunk (4 substep + chunk of substep) of load k of NL, and load of a chunk
+  static constexpr int pos(int k, int nl) { return k * 16 / nl; }
+  static constexpr int load_at(int p, int nl) {
+    for (int k = 0; k < nl; ++k)
+      if (pos(k, nl) == p) return k;
+    return -1;
+  }
+  static constexpr int BARRIER = 12;            // chunk 0 of substep 3
 };
 
 // K-loop over `ntiles` stages; src(t, ws, xs, k0) names the operands and K
@@ -269,6 +275,223 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
                                             int tid, int wn, int wm, uint32_t keep = 0) {
   static_assert(C::NW == 4 && C::FN == 4 && C::FM >= 2 && C::FM <= 4, "four waves of 128 x (64, 96 or 128)");
   using R = WideRing<C>;
+  if (ntiles <= 0) return;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
+  const int rl = lane & 31, ch = lane >> 5;
+  const bool wside = wave < 2;
+
+  bf16x8 fa[2][C::FN], fb[2][C::FM];
+  // chunks at or past kdim and masked activation rows enter as zero
+  auto fix = [&](int k0, int s, int buf) __attribute__((always_inline)) {
+    if (k0 + (2 * s + ch) * 8 >= kdim) {
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) fa[buf][i] = bf16x8{};
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) fb[buf][j] = bf16x8{};
+    }
+    if constexpr (MASK_ROWS) {
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j)
+        if (!((keep >> j) & 1u)) fb[buf][j] = bf16x8{};
+    }
+  };
+  auto mfma = [&](int buf, int i, int j) __attribute__((always_inline)) {
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[buf][i], fb[buf][j], acc[i][j], 0, 0, 0);
+  };
+  auto lds_sync = []() __attribute__((always_inline)) {   // own LDS writes done, then meet
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  };
+
+  // The waves of each side run the loop with their own number of loads, so
+  // that no load sits under a run-time branch (the compiler's wait counts for
+  // the staged registers stay exact).
+  auto body = [&](auto nlc) __attribute__((always_inline)) {
+    constexpr int NL = decltype(nlc)::value;
+    const int q0 = wside ? wave * R::PWW : C::TN / 8 + (wave - 2) * R::PWX;   // first 8-row group of the wave
+    // each lane's offset within a stage: row of its side, swizzled chunk
+    uint32_t lb[NL];
+    {
+      Side w, x;
+      int k0;
+      src(0, w, x, k0);
+      const uint32_t ld = wside ? w.ld_bytes : x.ld_bytes;
+#pragma unroll
+      for (int q = 0; q < NL; ++q) {
+        const int r = (q0 + q) * 8 + (lane >> 3) - (wside ? 0 : C::TN);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        lb[q] = uint32_t(r) * ld + uint32_t(c) * 16u;
+      }
+    }
+    struct Stage {
+      __amdgpu_buffer_rsrc_t res;
+      uint32_t add;
+    };
+    // stage t's operand and uniform offset; past the last stage an offset
+    // beyond every operand, so the loads return zeros and move no data
+    auto stage = [&](int t) __attribute__((always_inline)) {
+      Side w, x;
+      int k0;
+      src(t < ntiles ? t : ntiles - 1, w, x, k0);
+      const Side& sd = wside ? w : x;
+      const uint64_t base = uint64_t(uint32_t(sd.res[0])) | (uint64_t(uint32_t(sd.res[1]) & 0xFFFFu) << 32);
+      return Stage{__builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, sd.res[2], 0x00020000),
+                   t < ntiles ? uint32_t(sd.row0) * sd.ld_bytes + uint32_t(k0) * 2u : kMaskedOffset};
+    };
+    u32x4 stg[NL];
+    const uint32_t wofs = uint32_t(q0) * 1024u + uint32_t(lane) * 16u;
+    auto gload = [&](int k, const Stage& g) __attribute__((always_inline)) {
+      stg[k] = __builtin_amdgcn_raw_buffer_load_b128(g.res, lb[k] + g.add, 0, 0);
+    };
+    auto lwrite = [&](int k, char* slot) __attribute__((always_inline)) {
+      *reinterpret_cast<u32x4*>(slot + wofs + k * 1024) = stg[k];
+    };
+    // prologue: stage 0 in slot 0; stage 1 in registers, the loads after the
+    // barrier already written to slot 1 and holding stage 2
+    {
+      const Stage g0 = stage(0);
+#pragma unroll
+      for (int k = 0; k < NL; ++k) gload(k, g0);
+#pragma unroll
+      for (int k = 0; k < NL; ++k) lwrite(k, smem);
+      const Stage g1 = stage(1), g2 = stage(2);
+#pragma unroll
+      for (int k = 0; k < NL; ++k) gload(k, g1);
+#pragma unroll
+      for (int k = 0; k < NL; ++k)
+        if (R::pos(k, NL) > R::BARRIER) {
+          lwrite(k, smem + R::STAGE);
+          gload(k, g2);
+        }
+      lds_sync();
+    }
+#pragma unroll
+    for (int i = 0; i < C::FN; ++i) fa[0][i] = read_frag(smem, wrow + i * 32 + rl, ch);
+#pragma unroll
+    for (int j = 0; j < C::FM; ++j) fb[0][j] = read_frag(smem + C::TN * ROW_BYTES, xrow + j * 32 + rl, ch);
+
+    auto iter = [&](int t, auto checked, auto parity) __attribute__((always_inline)) {
+      constexpr bool CHECKED = decltype(checked)::value;
+      constexpr int P = decltype(parity)::value;   // t & 1
+      int k0 = 0;
+      if constexpr (CHECKED) {
+        Side w, x;
+        src(t, w, x, k0);
+      }
+      const Stage g2 = stage(t + 2), g3 = stage(t + 3);
+      char* const other = smem + (P ^ 1) * R::STAGE;
+      char* const mine = smem + P * R::STAGE;
+      auto substep = [&](auto sc) __attribute__((always_inline)) {
+        constexpr int s = decltype(sc)::value;
+        constexpr int buf = s & 1, ns = s < 3 ? s + 1 : 0, nb = (s + 1) & 1;
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (CHECKED) fix(k0, s, buf);
+        // the next substep's fragments: this stage's, or stage t+1's first (past
+        // the last stage a stale slot, never used)
+        const char* nx = smem + ((s < 3 ? P : P + 1) & 1) * R::STAGE;
+        auto chunk = [&](auto gc) __attribute__((always_inline)) {
+          constexpr int g = decltype(gc)::value;
+          constexpr int p = 4 * s + g;
+          constexpr int k = R::load_at(p, NL);
+          constexpr bool LOAD = k >= 0;
+          constexpr int kk = LOAD ? k : 0;
+          auto pair_write = [&]() __attribute__((always_inline)) {
+            if constexpr (LOAD) lwrite(kk, p > R::BARRIER ? mine : other);
+          };
+          auto pair_load = [&]() __attribute__((always_inline)) {
+            if constexpr (LOAD) gload(kk, p > R::BARRIER ? g3 : g2);
+          };
+          if constexpr (p == R::BARRIER) {
+            mfma(buf, 0, 0);
+            pair_write();
+            mfma(buf, 0, 1);
+            pair_load();
+#pragma unroll
+            for (int j = 2; j < C::FM; ++j) mfma(buf, 0, j);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_sync();   // stage t+1 is in its slot; no wave reads stage t's any more
+            __builtin_amdgcn_sched_barrier(0);
+            fa[nb][0] = read_frag(nx, wrow + rl, 2 * ns + ch);
+            fb[nb][0] = read_frag(nx + C::TN * ROW_BYTES, xrow + rl, 2 * ns + ch);
+            __builtin_amdgcn_sched_barrier(0);
+            return;
+          }
+          // the chunk's MFMAs (one row block against the wave's FM column
+          // blocks), a fragment read of the next substep after each of the
+          // first two, and the chunk's load pair
+          constexpr bool XREAD = g < C::FM;
+          mfma(buf, g, 0);
+          fa[nb][g] = read_frag(nx, wrow + g * 32 + rl, 2 * ns + ch);
+          mfma(buf, g, 1);
+          if constexpr (XREAD) fb[nb][g] = read_frag(nx + C::TN * ROW_BYTES, xrow + g * 32 + rl, 2 * ns + ch);
+          if constexpr (C::FM > 2) mfma(buf, g, 2);
+          pair_write();
+          if constexpr (C::FM > 3) mfma(buf, g, 3);
+          pair_load();
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);   // MFMA
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);   // LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (XREAD) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          if constexpr (C::FM > 2) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (LOAD) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);   // LDS write
+          if constexpr (C::FM > 3) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          if constexpr (LOAD) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);   // global load
+          __builtin_amdgcn_sched_barrier(0);
+        };
+        chunk(std::integral_constant<int, 0>{});
+        chunk(std::integral_constant<int, 1>{});
+        chunk(std::integral_constant<int, 2>{});
+        chunk(std::integral_constant<int, 3>{});
+      };
+      substep(std::integral_constant<int, 0>{});
+      substep(std::integral_constant<int, 1>{});
+      substep(std::integral_constant<int, 2>{});
+      substep(std::integral_constant<int, 3>{});
+    };
+    // Stages go in pairs, so that the ring slot a fragment read addresses is a
+    // compile-time constant (its address then needs no per-stage arithmetic).
+    // The K tail can only fall in the last stage of the base product; the
+    // expand (MASK_ROWS) checks every stage.
+    using P0 = std::integral_constant<int, 0>;
+    using P1 = std::integral_constant<int, 1>;
+    int t = 0;
+    if constexpr (!MASK_ROWS) {
+      for (; t + 2 < ntiles; t += 2) {
+        iter(t, std::false_type{}, P0{});
+        iter(t + 1, std::false_type{}, P1{});
+      }
+    }
+    for (; t + 1 < ntiles; t += 2) {
+      iter(t, std::true_type{}, P0{});
+      iter(t + 1, std::true_type{}, P1{});
+    }
+    if (t < ntiles) iter(t, std::true_type{}, P0{});
+  };
+  if constexpr (R::PWX == R::PWW) {
+    body(std::integral_constant<int, R::PWW>{});
+  } else {
+    if (wside) body(std::integral_constant<int, R::PWW>{});
+    else body(std::integral_constant<int, R::PWX>{});
+  }
+  // the loads past the last stage (zeros) and the last writes are done before
+  // the ring is reused by whatever runs next
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
+}
+
+// The same K-loop with the loads written straight into LDS (buffer_load ...
+// lds), for the expand: its few stages, with the row masks and a per-adapter
+// operand per call, would push the register-staged loop into spills.  A wave's
+// 16 (or 12, 8) loads of a stage go out in groups of four under one M0 value:
+// groups 0 and 1 of stage t+2 right after the barrier in substep 3 of stage t,
+// groups 2 and 3 in substep 0 of stage t+1, after its 12th and 16th MFMA.
+template <class C, bool MASK_ROWS, class Src>
+__device__ __forceinline__ void k_loop_wide_dma(f32x16 (&acc)[C::FN][C::FM], int ntiles, int kdim, Src src,
+                                                char* smem, int tid, int wn, int wm, uint32_t keep = 0) {
+  static_assert(C::NW == 4 && C::FN == 4 && C::FM >= 2 && C::FM <= 4, "four waves of 128 x (64, 96 or 128)");
+  using R = WideRing<C>;
+  static_assert(R::PWX % 4 == 0, "load groups of four");
   if (ntiles <= 0) return;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
@@ -711,7 +934,7 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       const Side tl{tres, tld, lo_row0, 0, 0};
       const int nr = 2 * ((ra + BK - 1) / BK);
       auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
-      k_loop_wide<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
+      k_loop_wide_dma<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
     }
   }
 
