@@ -77,3 +77,21 @@ def test_tile_height_gaussian(tm):
     base = np.repeat(np.array(p.seg_adapter) < 0, np.diff(p.seg_starts))
     y0 = y_to_numpy(run(p, seg_adapter=[-1] * len(p.seg_adapter)))
     assert np.array_equal(y[base], y0[base])
+
+
+@pytest.mark.parametrize("tm", sorted(CASES))
+@pytest.mark.parametrize("K", [64, 72, 128, 200])
+def test_tile_height_few_stages(tm, K):
+    """One to four 64-wide K stages (the 72 and 200 with a K tail): the loads that a short loop
+    issues past its last stage must read zeros and land nowhere that a stage reads.  Integer
+    inputs, exact."""
+    c = dict(CASES[tm], K=K)
+    starts, labels = table(93 + tm + K, c["M"])
+    p = synth.random_problem(94, scale=[1.0, 0.5, -2.0], integer=True, rank=48, seg_starts=starts,
+                             seg_adapter=labels, n_adapters=3, **c)
+    assert bd.tile_rows(p.M, p.N, p.K) == tm
+    log(f"case tile {tm} K={K} exact M={p.M} N={p.N}")
+    exact = lora_proj_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale)
+    y32 = y_to_numpy(run(p, dtype="bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
