@@ -39,16 +39,14 @@ namespace {
 // per CU per cycle).
 constexpr int BK = 64;
 constexpr int ROW_BYTES = BK * 2;
-constexpr int NSTAGE = 4;       // LDS ring depth of the shrink; NSTAGE - 1 stages are in flight
 
 // One operand of a K-loop: rows of a row-major bf16 matrix whose reduction
-// index is contiguous.  Tile row i is global row row0 + i.  Rows past the
-// operand's extent are never fetched; rows outside [lo, hi) are zeroed in the
-// MFMA operands when the loop masks rows.
+// index is contiguous.  Tile row i is global row row0 + i; rows past the
+// operand's extent (its descriptor's size) load as zeros.
 struct Side {
   i32x4 res;
   uint32_t ld_bytes;
-  int32_t row0, lo, hi;
+  int32_t row0;
 };
 
 // Tile shapes.  TN x TM output tile (TN weight rows, TM activation rows),
@@ -73,55 +71,14 @@ struct Tile {
 // all 64 banks.
 __device__ __forceinline__ int lds_off(int r, int c) { return r * ROW_BYTES + ((c ^ ((r >> 1) & 7)) << 4); }
 
-// Wait until at most `stages` later stages of PW loads each are still in flight.
-template <int PW>
-__device__ __forceinline__ void wait_stages(int stages) {
-  static_assert(PW * (NSTAGE - 2) <= 63, "vmcnt holds at most 63");
-  if (stages >= 3 && NSTAGE > 4) wait_vm<PW * (NSTAGE > 4 ? 3 : 0)>();
-  else if (stages >= 2) wait_vm<2 * PW>();
-  else if (stages == 1) wait_vm<PW>();
-  else wait_vm<0>();
-}
-
-// A wave's PW loads of a stage are consecutive 8-row groups of one side (the
-// weight rows come first and fill whole waves), so they go out in groups of up
-// to four under one M0 value.  GATHER: the activation side's loads start at
-// the per-lane byte offsets gx[] (gather_offsets).  A row with no X row behind
-// it starts at kGatherMasked: past every operand (each under 2 GiB) even after
-// a load group's bias of up to 3 KiB, so it loads zeros, and with more than 128
-// rows a row of X is under 17 MB, so adding the K offset cannot wrap.  (A
-// compare and select per load here cost 0.6% of a 16k call.)
 constexpr uint32_t kGatherMasked = 0x80001000u;
-template <class C, bool GATHER = false>
-__device__ __forceinline__ void issue_stage(char* stage, const Side& ws, const Side& xs, int k0, int wave, int lane,
-                                            const uint32_t* gx = nullptr) {
-  static_assert((C::TN / 8) % C::PW == 0, "a wave's groups must lie on one side");
-  constexpr int NG = C::PW < 4 ? C::PW : 4;
-  static_assert(C::PW % NG == 0, "groups of loads must split evenly");
-  const uint32_t base = lds_addr(stage);
-  const int g0 = wave * C::PW;                      // first 8-row group of the wave (uniform)
-  const bool wside = g0 * 8 < C::TN;
-  const Side& sd = wside ? ws : xs;
-#pragma unroll
-  for (int q = 0; q < C::PW; q += NG) {
-    uint32_t off[NG];
-#pragma unroll
-    for (int i = 0; i < NG; ++i) {
-      const int r = (g0 + q + i) * 8 + (lane >> 3) - (wside ? 0 : C::TN);
-      const int c = (lane & 7) ^ ((r >> 1) & 7);
-      if (GATHER && !wside) {
-        off[i] = gx[q + i] + uint32_t(k0) * 2u;
-      } else {
-        off[i] = uint32_t(sd.row0 + r) * sd.ld_bytes + uint32_t(k0 + c * 8) * 2u;
-      }
-    }
-    dma16_group<NG>(sd.res, off, base + uint32_t(g0 + q) * 1024u);
-  }
-}
 
-// The activation-side offsets of issue_stage<C, true> for this lane, from the
-// row map xrows (LDS, -1 for none): row * ld + the lane's swizzled chunk, the
-// same for every stage.  Weight-side waves get none.
+// The shrink's activation-side load offsets for this lane, from the row map
+// xrows (LDS, -1 for none): row * ld + the lane's swizzled chunk, the same for
+// every stage.  A row with no X row behind it starts at kGatherMasked, past
+// every operand (each under 2 GiB), so it loads zeros; with more than 128 rows
+// a row of X is under 17 MB, so adding the K offset cannot wrap.  (A compare
+// and select per load cost 0.6% of a 16k call.)
 template <class C>
 __device__ __forceinline__ void gather_offsets(uint32_t (&gx)[C::PW], const int* xrows, uint32_t ld_bytes, int wave,
                                                int lane) {
@@ -139,96 +96,125 @@ __device__ __forceinline__ bf16x8 read_frag(const char* base, int r, int c) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(base + lds_off(r, c)));
 }
 
-// acc += (weight tile) x (activation tile)^T over one stage (BK / 16 k16
-// substeps).  MASK_ROWS zeroes activation rows outside [lo, hi); TAIL zeroes
-// the chunks at or past kdim on both sides.
-template <class C, bool MASK_ROWS, bool TAIL>
-__device__ __forceinline__ void mma_stage(f32x16 (&acc)[C::FN][C::FM], const char* wt, const char* xt, int wrow,
-                                          int xrow, int lane, int xg0, int lo, int hi, int k0, int kdim) {
-#pragma unroll
-  for (int s = 0; s < BK / 16; ++s) {
-    const int c = 2 * s + (lane >> 5);
-    bf16x8 a[C::FN], b[C::FM];
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i) a[i] = read_frag(wt, wrow + i * 32 + (lane & 31), c);
-#pragma unroll
-    for (int j = 0; j < C::FM; ++j) b[j] = read_frag(xt, xrow + j * 32 + (lane & 31), c);
-    if constexpr (TAIL) {
-      if (k0 + c * 8 >= kdim) {
-#pragma unroll
-        for (int i = 0; i < C::FN; ++i) a[i] = bf16x8{};
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j) b[j] = bf16x8{};
-      }
-    }
-    if constexpr (MASK_ROWS) {
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j) {
-        const int grow = xg0 + xrow + j * 32 + (lane & 31);
-        if (grow < lo || grow >= hi) b[j] = bf16x8{};
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < C::FN; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FM; ++j)
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-  }
-}
-
-// K-loop over `ntiles` stages.  src(t, ws, xs, k0) names the weight-side and
-// activation-side operands and the K offset of stage t; stages from `ntail` on
-// reach past kdim and have their out-of-range chunks zeroed.  Stage t lives in
-// ring slot t % NSTAGE; the loads of stages t+1 .. t+NSTAGE-2 stay in flight
-// while stage t is consumed.  With MASK_ROWS the activation rows outside the
-// activation side's [lo, hi) enter the MFMAs as zero.
-template <class C, bool MASK_ROWS, bool TAIL, bool GATHER, class Src>
-__device__ __forceinline__ void k_stages(f32x16 (&acc)[C::FN][C::FM], int t0, int t1, int ntiles, int kdim, Src& src,
-                                         char* smem, int wave, int lane, int wrow, int xrow, const uint32_t* gx) {
-  for (int t = t0; t < t1; ++t) {
-    // stage t has landed once at most the loads of the stages issued after it remain
-    wait_stages<C::PW>(min(NSTAGE - 2, ntiles - 1 - t));
-    __syncthreads();
-    if (t + NSTAGE - 1 < ntiles) {   // refill the slot every wave finished reading in stage t-1
-      Side ws, xs;
-      int k0;
-      src(t + NSTAGE - 1, ws, xs, k0);
-      issue_stage<C, GATHER>(smem + ((t + NSTAGE - 1) % NSTAGE) * C::STAGE, ws, xs, k0, wave, lane, gx);
-    }
-    Side ws, xs;
-    int k0;
-    src(t, ws, xs, k0);
-    const char* cur = smem + (t % NSTAGE) * C::STAGE;
-    mma_stage<C, MASK_ROWS, TAIL>(acc, cur, cur + C::TN * ROW_BYTES, wrow, xrow, lane, xs.row0, xs.lo, xs.hi, k0,
-                                  kdim);
-  }
-}
-
-template <class C, bool MASK_ROWS, bool GATHER = false, class Src>
-__device__ __forceinline__ void k_loop(f32x16 (&acc)[C::FN][C::FM], int ntiles, int ntail, int kdim, Src src,
-                                       char* smem, int tid, int wn, int wm, const int* xrows = nullptr) {
+// Register-staged K-loop of the shrink: a ring of two LDS slots, each lane's 8
+// loads of a stage in VGPRs two stages ahead (two register sets).  In stage t
+// the wave writes stage t+1 (set (t+1) & 1) into the other slot and loads
+// stage t+3 into the same registers, two load pairs per substep; one barrier
+// ends the stage.  The activation side's offsets come from the row map
+// (gather_offsets); stages past the last read at an offset past the operands.
+template <class C, class Src>
+__device__ __forceinline__ void k_loop_small_reg(f32x16 (&acc)[C::FN][C::FM], int ntiles, int ntail, int kdim,
+                                                 Src src, char* smem, int tid, int wn, int wm, const int* xrows) {
+  static_assert(C::PW == 8 && C::FN * C::FM == 4, "128 x 128 tiles of four waves");
   if (ntiles <= 0) return;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wrow = wn * (C::TN / C::WN), xrow = wm * (C::TM / C::WM);
-  uint32_t gx[C::PW] = {};
-  if constexpr (GATHER) {
+  const int g0 = wave * C::PW;
+  const bool wside = g0 * 8 < C::TN;
+  uint32_t lb[C::PW];
+  __amdgpu_buffer_rsrc_t res;
+  {
     Side ws, xs;
     int k0;
     src(0, ws, xs, k0);
-    gather_offsets<C>(gx, xrows, xs.ld_bytes, wave, lane);
-  }
+    if (wside) {
 #pragma unroll
-  for (int p = 0; p < NSTAGE - 1; ++p) {
-    if (p < ntiles) {
-      Side ws, xs;
-      int k0;
-      src(p, ws, xs, k0);
-      issue_stage<C, GATHER>(smem + p * C::STAGE, ws, xs, k0, wave, lane, gx);
+      for (int k = 0; k < C::PW; ++k) {
+        const int r = (g0 + k) * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ ((r >> 1) & 7);
+        lb[k] = uint32_t(ws.row0 + r) * ws.ld_bytes + uint32_t(c) * 16u;
+      }
+    } else {
+      gather_offsets<C>(lb, xrows, xs.ld_bytes, wave, lane);
     }
+    const Side& sd = wside ? ws : xs;
+    const uint64_t b = uint64_t(uint32_t(sd.res[0])) | (uint64_t(uint32_t(sd.res[1]) & 0xFFFFu) << 32);
+    res = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b), (short)0, sd.res[2], 0x00020000);
   }
-  k_stages<C, MASK_ROWS, false, GATHER>(acc, 0, ntail, ntiles, kdim, src, smem, wave, lane, wrow, xrow, gx);
-  k_stages<C, MASK_ROWS, true, GATHER>(acc, ntail, ntiles, ntiles, kdim, src, smem, wave, lane, wrow, xrow, gx);
-  __syncthreads();   // the ring is reused by whatever runs next
+  // stage t's uniform offset; past the last stage one past every operand (the
+  // data is never used)
+  auto add = [&](int t) __attribute__((always_inline)) {
+    Side ws, xs;
+    int k0;
+    src(t < ntiles ? t : 0, ws, xs, k0);
+    return t < ntiles ? uint32_t(k0) * 2u : kMaskedOffset;
+  };
+  u32x4 stg[2][C::PW];
+  const uint32_t wofs = uint32_t(g0) * 1024u + uint32_t(lane) * 16u;
+  auto gload = [&](int set, int k, uint32_t a) __attribute__((always_inline)) {
+    stg[set][k] = __builtin_amdgcn_raw_buffer_load_b128(res, lb[k] + a, 0, 0);
+  };
+  auto lwrite = [&](int set, int k, char* slot) __attribute__((always_inline)) {
+    *reinterpret_cast<u32x4*>(slot + wofs + k * 1024) = stg[set][k];
+  };
+  auto lds_sync = []() __attribute__((always_inline)) {
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+  };
+  {
+    const uint32_t a0 = add(0), a1 = add(1), a2 = add(2);
+#pragma unroll
+    for (int k = 0; k < C::PW; ++k) gload(0, k, a0);
+#pragma unroll
+    for (int k = 0; k < C::PW; ++k) gload(1, k, a1);
+#pragma unroll
+    for (int k = 0; k < C::PW; ++k) {
+      lwrite(0, k, smem);
+      gload(0, k, a2);
+    }
+    lds_sync();
+  }
+  auto stage = [&](int t, auto tailc, auto par) __attribute__((always_inline)) {
+    constexpr bool TAIL = decltype(tailc)::value;
+    constexpr int P = decltype(par)::value;   // t & 1
+    constexpr int SET = P ^ 1;                // registers of stage t+1
+    Side ws, xs;
+    int k0;
+    src(t, ws, xs, k0);
+    const uint32_t a3 = add(t + 3);
+    const char* cur = smem + P * C::STAGE;
+    char* const nxt = smem + (P ^ 1) * C::STAGE;
+#pragma unroll
+    for (int s = 0; s < BK / 16; ++s) {
+      const int c = 2 * s + (lane >> 5);
+      bf16x8 fa[C::FN], fb[C::FM];
+#pragma unroll
+      for (int i = 0; i < C::FN; ++i) fa[i] = read_frag(cur, wrow + i * 32 + (lane & 31), c);
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) fb[j] = read_frag(cur + C::TN * ROW_BYTES, xrow + j * 32 + (lane & 31), c);
+      if constexpr (TAIL) {
+        if (k0 + c * 8 >= kdim) {
+#pragma unroll
+          for (int i = 0; i < C::FN; ++i) fa[i] = bf16x8{};
+#pragma unroll
+          for (int j = 0; j < C::FM; ++j) fb[j] = bf16x8{};
+        }
+      }
+      acc[0][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[0], acc[0][0], 0, 0, 0);
+      lwrite(SET, 2 * s, nxt);
+      acc[0][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[0], fb[1], acc[0][1], 0, 0, 0);
+      gload(SET, 2 * s, a3);
+      acc[1][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[0], acc[1][0], 0, 0, 0);
+      lwrite(SET, 2 * s + 1, nxt);
+      acc[1][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[1], fb[1], acc[1][1], 0, 0, 0);
+      gload(SET, 2 * s + 1, a3);
+    }
+    lds_sync();   // stage t+1 is in its slot; no wave reads stage t's any more
+  };
+  using P0 = std::integral_constant<int, 0>;
+  using P1 = std::integral_constant<int, 1>;
+  int t = 0;
+  for (; t + 1 < ntail; t += 2) {
+    stage(t, std::false_type{}, P0{});
+    stage(t + 1, std::false_type{}, P1{});
+  }
+  for (; t + 1 < ntiles; t += 2) {
+    stage(t, std::true_type{}, P0{});
+    stage(t + 1, std::true_type{}, P1{});
+  }
+  if (t < ntiles) stage(t, std::true_type{}, P0{});
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+  __syncthreads();
 }
 
 // ------------------------------------------------------------------ output K-loop
@@ -785,7 +771,7 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
                                                        int ntm) {
   static_assert(C::TM == kShrinkRows && C::TN == kShrinkRows, "shrink tiles are planned in kShrinkRows rows");
   static_assert(C::NW * C::FN * C::FM * 4 * 1024 == int(kShrinkPartBytes), "partial layout");
-  __shared__ __attribute__((aligned(1024))) char smem[NSTAGE * C::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * C::STAGE];
   __shared__ int phys[C::TM];
   const int ntiles = ntn * ntm;
   const int lt = int(blockIdx.x) % ntiles, split = int(blockIdx.x) / ntiles;
@@ -797,8 +783,8 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
   shrink_rows<C>(phys, st, tl.a, tl.v0, tl.nrows, tid);
   __syncthreads();
 
-  const Side as{make_rsrc_words(at.A[tl.a], at.a_bytes[tl.a]), uint32_t(p.K) * 2u, tl.j0, 0, atrank};
-  const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, 0, 0, 0};
+  const Side as{make_rsrc_words(at.A[tl.a], at.a_bytes[tl.a]), uint32_t(p.K) * 2u, tl.j0};
+  const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, 0};
   f32x16 acc[C::FN][C::FM];
 #pragma unroll
   for (int i = 0; i < C::FN; ++i)
@@ -808,9 +794,9 @@ __global__ __launch_bounds__(C::NT) void shrink_kernel(ProjArgs p, SegTable st, 
   const int nk = (p.K + BK - 1) / BK;
   const int t0 = split * nk / sp.splits, t1 = (split + 1) * nk / sp.splits;
   const int nfull = p.K / BK;
-  k_loop<C, false, true>(acc, t1 - t0, max(0, min(t1, nfull) - t0), p.K,
-                         [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = (t0 + t) * BK; },
-                         smem, tid, wn, wm, phys);
+  k_loop_small_reg<C>(acc, t1 - t0, max(0, min(t1, nfull) - t0), p.K,
+                      [&](int t, Side& ws, Side& xsd, int& k0) { ws = as; xsd = xs; k0 = (t0 + t) * BK; },
+                      smem, tid, wn, wm, phys);
   if (sp.splits == 1) {
     store_t<C>(acc, p, at.scale[tl.a], tl.j0, phys, wn, wm, lane);
     return;
@@ -898,8 +884,8 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
 
   // base product over K
   {
-    const Side ws{make_rsrc_words(p.W, p.w_bytes), uint32_t(p.K) * 2u, n0, 0, p.N};
-    const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0, 0, p.M};
+    const Side ws{make_rsrc_words(p.W, p.w_bytes), uint32_t(p.K) * 2u, n0};
+    const Side xs{make_rsrc_words(p.X, p.x_bytes), uint32_t(p.K) * 2u, m0};
     const int nk = (p.K + BK - 1) / BK;
     auto src = [&](int t, Side& w, Side& x, int& k0) { w = ws; x = xs; k0 = t * BK; };
     k_loop_wide<C, false>(acc, nk, p.K, src, smem, tid, wn, wm);
@@ -929,9 +915,9 @@ __global__ __launch_bounds__(C::NT) __attribute__((amdgpu_waves_per_eu(1, 1))) v
       const int ra = at.rank[a];
       const uint32_t ld = uint32_t(ra) * 2u, tcol = uint32_t(slice * ra) * 2u;
       const i32x4 tres = make_rsrc_words(static_cast<const char*>(p.T) + tcol, p.t_bytes - tcol);
-      const Side bs{make_rsrc_words(at.B[a], at.b_bytes[a]), ld, n0, 0, p.N};
-      const Side th{tres, tld, m0, 0, 0};
-      const Side tl{tres, tld, lo_row0, 0, 0};
+      const Side bs{make_rsrc_words(at.B[a], at.b_bytes[a]), ld, n0};
+      const Side th{tres, tld, m0};
+      const Side tl{tres, tld, lo_row0};
       const int nr = 2 * ((ra + BK - 1) / BK);
       auto src = [&](int t, Side& w, Side& x, int& k0) { w = bs; x = (t & 1) ? tl : th; k0 = (t >> 1) * BK; };
       k_loop_wide_dma<C, true>(acc, nr, ra, src, smem, tid, wn, wm, keep);
