@@ -38,6 +38,24 @@ def test_noalloc_equals_lora_proj_on_two_calls():
                                                               p.scale))
 
 
+def test_noalloc_split_shrink():
+    """A prefill call whose shrink splits over K (4 splits: its fp32 partials sit in the array after
+    T), then a call that does not split: each bitwise equal to lora_proj."""
+    import torch
+    calls = [dict(M=300, N=520, K=2056, rank=48, seg_starts=[0, 40, 41, 200, 300], seg_adapter=[0, -1, 1, 0],
+                  n_adapters=2, scale=0.5),
+             dict(CALLS[0])]
+    for i, c in enumerate(calls):
+        p = synth.random_problem(98 + i, **c)
+        log(f"case noalloc split call {i} M={p.M} K={p.K}")
+        X, W, A, B = to_device(p)
+        ref = bd.lora_proj(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale)
+        out = torch.empty((p.M, p.N), dtype=torch.bfloat16, device="cuda")
+        y = bd.lora_proj_noalloc(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(y_bits(y), y_bits(ref))
+
+
 def test_noalloc_repeated_decode_calls_stay_exact():
     """Integer inputs: several decode calls in a row on the one array (each clears its counters),
     every one exact."""
