@@ -8,20 +8,22 @@
 //           adapter a).  T is stored as
 //           two bf16 halves, hi = bf16(T) and lo = bf16(T - hi), so the expand
 //           can run on bf16 MFMA while keeping T to about 2^-17 relative.
+//           When its tile grid is small the shrink splits K over several
+//           blocks per tile, and a third launch sums their partials.
 //   main    per output tile: acc = X W^T over K, then, if the tile holds adapter
 //           rows, acc += T_hi B_a^T + T_lo B_a^T over the rank (rows of other
 //           segments read as zero), then one round-to-nearest-even store.
 //
-// Both run LDS-staged MFMA K-loops: K slabs move from global memory straight
-// into a ring of LDS stages (buffer_load ... lds, 16 bytes per lane), an XOR
-// swizzle on 16-byte chunks keeps ds_read_b128 conflict-free, and
-// v_mfma_f32_32x32x16_bf16 accumulates in fp32.  Slabs are 64 elements of K
-// (one whole 128-byte line per row); the shrink keeps a ring of four, the main
-// kernel a ring of two, with four waves of 128 x 128 that keep their
-// accumulators in AGPRs.  The MFMA "A" operand is the weight side
-// (rows n) and "B" is the activation side (rows m), so each lane ends with
-// four consecutive output columns of one row and stores them as one 8-byte
-// write.
+// Both run MFMA K-loops over a ring of LDS stages: slabs of 64 elements of K
+// (one whole 128-byte line per row), loaded 16 bytes per lane into registers a
+// stage or two ahead and written to the ring with ds_write_b128 (the expand
+// loads straight into LDS with buffer_load ... lds).  An XOR swizzle on
+// 16-byte chunks keeps the ds_read_b128 fragment reads conflict-free, and
+// v_mfma_f32_32x32x16_bf16 accumulates in fp32.  The main kernel runs four
+// waves of 128 x 128 that keep their accumulators in AGPRs.  The MFMA "A"
+// operand is the weight side (rows n) and "B" is the activation side (rows m),
+// so each lane ends with four consecutive output columns of one row and
+// stores them as one 8-byte write.
 //
 // Every global access goes through a buffer descriptor sized to its operand:
 // masked or out-of-range loads return zero and out-of-range stores are
