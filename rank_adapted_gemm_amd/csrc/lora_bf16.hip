@@ -103,7 +103,9 @@ __device__ __forceinline__ bf16x8 read_frag(const char* base, int r, int c) {
 // the wave writes stage t+1 (set (t+1) & 1) into the other slot and loads
 // stage t+3 into the same registers, two load pairs per substep; one barrier
 // ends the stage.  The activation side's offsets come from the row map
-// (gather_offsets); stages past the last read at an offset past the operands.
+// (gather_offsets).  The loads of stages past the last bring data that no
+// stage reads: at an offset past the operands, or, for a row with no X row
+// behind it, one that wraps to an offset inside X.
 template <class C, class Src>
 __device__ __forceinline__ void k_loop_small_reg(f32x16 (&acc)[C::FN][C::FM], int ntiles, int ntail, int kdim,
                                                  Src src, char* smem, int tid, int wn, int wm, const int* xrows) {
@@ -129,12 +131,10 @@ __device__ __forceinline__ void k_loop_small_reg(f32x16 (&acc)[C::FN][C::FM], in
     } else {
       gather_offsets<C>(lb, xrows, xs.ld_bytes, wave, lane);
     }
-    const Side& sd = wside ? ws : xs;
-    const uint64_t b = uint64_t(uint32_t(sd.res[0])) | (uint64_t(uint32_t(sd.res[1]) & 0xFFFFu) << 32);
-    res = __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(b), (short)0, sd.res[2], 0x00020000);
+    res = rsrc_of_words(wside ? ws.res : xs.res);
   }
-  // stage t's uniform offset; past the last stage one past every operand (the
-  // data is never used)
+  // stage t's uniform offset; past the last stage kMaskedOffset (the data is
+  // never used)
   auto add = [&](int t) __attribute__((always_inline)) {
     Side ws, xs;
     int k0;
@@ -323,9 +323,7 @@ __device__ __forceinline__ void k_loop_wide(f32x16 (&acc)[C::FN][C::FM], int nti
       int k0;
       src(t < ntiles ? t : ntiles - 1, w, x, k0);
       const Side& sd = wside ? w : x;
-      const uint64_t base = uint64_t(uint32_t(sd.res[0])) | (uint64_t(uint32_t(sd.res[1]) & 0xFFFFu) << 32);
-      return Stage{__builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, sd.res[2], 0x00020000),
-                   t < ntiles ? uint32_t(sd.row0) * sd.ld_bytes + uint32_t(k0) * 2u : kMaskedOffset};
+      return Stage{rsrc_of_words(sd.res), t < ntiles ? uint32_t(sd.row0) * sd.ld_bytes + uint32_t(k0) * 2u : kMaskedOffset};
     };
     u32x4 stg[NL];
     const uint32_t wofs = uint32_t(q0) * 1024u + uint32_t(lane) * 16u;

@@ -24,6 +24,12 @@ __device__ __forceinline__ i32x4 make_rsrc_words(const void* p, uint32_t bytes) 
   return i32x4{int32_t(uint32_t(a)), int32_t(uint32_t(a >> 32) & 0xFFFFu), int32_t(bytes), 0x00020000};
 }
 
+// The descriptor of make_rsrc_words as a buffer resource, for the builtin loads.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of_words(const i32x4& w) {
+  const uint64_t base = uint64_t(uint32_t(w[0])) | (uint64_t(uint32_t(w[1]) & 0xFFFFu) << 32);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(base), (short)0, w[2], 0x00020000);
+}
+
 // Global -> LDS: one buffer_load_dwordx4 with the lds flag writes 64 lanes x
 // 16 bytes contiguously at M0.  Issued from inline assembly (M0 is set in the
 // same statement), so completion is tracked by explicit vmcnt waits.
