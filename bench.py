@@ -28,6 +28,7 @@ Prints one JSON line on stdout; progress goes to stderr.
 from __future__ import annotations
 
 import argparse
+import contextlib
 import ctypes
 import hashlib
 import json
@@ -90,6 +91,64 @@ class HipEvents:
         for e in self.events:
             self.lib.hipEventDestroy(e)
         self.events = []
+
+
+# ------------------------------------------------------------------ clocks
+class ClockSampler:
+    """The GPU's current shader and memory clock levels, sampled every few milliseconds from a
+    thread while a timed region runs (the level marked '*' in the driver's pp_dpm_sclk and
+    pp_dpm_mclk files).  The driver reports DPM levels; the effective clock under load comes from
+    the counter profiles.  Where the files are missing, the summary is None."""
+
+    def __init__(self, period_s=0.004):
+        import glob
+        self.files = {}
+        for key in ("sclk", "mclk"):
+            paths = sorted(glob.glob(f"/sys/class/drm/card*/device/pp_dpm_{key}"))
+            if paths:
+                self.files[key] = paths[0]
+        self.period = period_s
+        self.samples = {k: [] for k in self.files}
+        self._stop = None
+        self._thread = None
+
+    def _read(self, path):
+        try:
+            for line in open(path):
+                if line.rstrip().endswith("*"):
+                    return int(line.split(":", 1)[1].strip().split("M")[0])
+        except (OSError, ValueError, IndexError):
+            pass
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            for k, path in self.files.items():
+                v = self._read(path)
+                if v is not None:
+                    self.samples[k].append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        import threading
+        if self.files:
+            self._stop = threading.Event()
+            self._thread = threading.Thread(target=self._run, daemon=True)
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        if self._thread is not None:
+            self._stop.set()
+            self._thread.join()
+        return False
+
+    def summary(self):
+        out = {}
+        for k, v in self.samples.items():
+            if v:
+                out[f"{k}_mhz"] = dict(median=int(np.median(v)), min=int(min(v)), max=int(max(v)), samples=len(v))
+        return out or None
 
 
 # ------------------------------------------------------------------ work model
@@ -193,7 +252,7 @@ class StepRunner:
                 raise bd.LoraError(st, bd.status_string(st))
 
 
-def time_steps(runner, steps, warmup, hip, events=True):
+def time_steps(runner, steps, warmup, hip, events=True, clocks=None):
     """Wall time of `steps` steps; with `events`, also each output kernel's duration.
 
     The decode stack is timed without events: a record costs a little time even without
@@ -205,11 +264,12 @@ def time_steps(runner, steps, warmup, hip, events=True):
     torch.cuda.synchronize()
     pairs = [[hip.pair() for _ in runner.calls] for _ in range(steps)] if events else [None] * steps
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for s in range(steps):
-        runner.step(events=pairs[s])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
+    with clocks if clocks is not None else contextlib.nullcontext():   # clock samples over the timed steps
+        t0 = time.perf_counter()
+        for s in range(steps):
+            runner.step(events=pairs[s])
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
     if not events:
         return wall, None
     main_ms = [[hip.elapsed_ms(a, b) for (a, b) in row] for row in pairs]
@@ -329,20 +389,27 @@ def run_prefill(a, dev, hip, name="prefill16k", steps=None, warmup=None):
     runner = StepRunner(layers, w["seg_starts"], w["seg_adapter"], w["scale"], dev)
     main_flops, shrink_flops, byts = runner.work()
     log(f"{name}: {warmup} warmup + {steps} timed steps of {len(runner.calls)} calls")
-    wall, main_ms = time_steps(runner, steps, warmup, hip)
+    clocks = ClockSampler()
+    wall, main_ms = time_steps(runner, steps, warmup, hip, clocks=clocks)
     ms_per_step = wall * 1e3 / steps
     step_flops = main_flops + shrink_flops
     value = step_flops / (ms_per_step / 1e3) / 1e12
     main_achieved = main_flops * steps / (main_ms.sum() / 1e3) / 1e12
     n7 = len(synth.projections(name))
     per_proj_ms = main_ms.reshape(steps, -1, n7).mean(axis=(0, 1))   # per projection, over layers and steps
+    by_proj = main_ms.reshape(steps, -1, n7).transpose(2, 0, 1).reshape(n7, -1)
     log(f"{name}: {ms_per_step:.3f} ms/step, {value:.1f} TFLOP/s; output kernel {main_achieved:.1f} TFLOP/s; "
         + ", ".join(f"{p['name']} {t:.3f}" for p, t in zip(runner.calls, per_proj_ms)))
     roofline = dict(bound="mfma", achieved=round(main_achieved, 2), peak=PEAK_BF16_TFLOPS, unit="TFLOP/s",
                     frac=round(main_achieved / PEAK_BF16_TFLOPS, 4), traffic=traffic_record(),
                     kernel="main_kernel<Tile<256,256,2,2>, bf16 out>",
                     launch_avg_ms=round(float(main_ms.mean()), 4),
-                    per_projection_ms={p["name"]: round(float(t), 4) for p, t in zip(runner.calls, per_proj_ms)})
+                    launch_median_ms=round(float(np.median(main_ms)), 4), launch_min_ms=round(float(main_ms.min()), 4),
+                    per_projection_ms={p["name"]: round(float(t), 4) for p, t in zip(runner.calls, per_proj_ms)},
+                    per_projection_median_ms={p["name"]: round(float(np.median(d)), 4)
+                                              for p, d in zip(runner.calls, by_proj)},
+                    per_projection_min_ms={p["name"]: round(float(d.min()), 4) for p, d in zip(runner.calls, by_proj)},
+                    clocks=clocks.summary())
     n_calls = len(runner.calls)
     del runner, layers
     torch.cuda.empty_cache()
@@ -484,7 +551,8 @@ def run_decode(a, dev, hip, grouped=False, q4=False):
         layers.append(calls)
     runner = StepRunner(layers, w5["seg_starts"], w5["seg_adapter"], w5["scale"], dev)
     dmain, dshrink, dbytes = runner.work()
-    wall5, _ = time_steps(runner, a.decode_steps, a.warmup, hip, events=False)
+    clocks = ClockSampler()
+    wall5, _ = time_steps(runner, a.decode_steps, a.warmup, hip, events=False, clocks=clocks)
     ms5 = wall5 * 1e3 / a.decode_steps
     gbs = dbytes / (ms5 / 1e3) / 1e9
     log(f"{tag}: {ms5:.3f} ms/step, {gbs:.0f} GB/s ({gbs / PEAK_HBM_GBS:.1%} of HBM)")
@@ -502,7 +570,7 @@ def run_decode(a, dev, hip, grouped=False, q4=False):
                 value=round(gbs, 1), unit="GB/s", frac=round(gbs / PEAK_HBM_GBS, 4),
                 ms_per_step=round(ms5, 4), bytes_per_step=dbytes, steps=a.decode_steps,
                 tflops=round((dmain + dshrink) / (ms5 / 1e3) / 1e12, 2),
-                calls_per_step=n_calls, call_avg_us=round(ms5 * 1e3 / n_calls, 2))
+                calls_per_step=n_calls, call_avg_us=round(ms5 * 1e3 / n_calls, 2), clocks=clocks.summary())
 
 
 def run_extract(a, dev):
@@ -653,7 +721,9 @@ def main(argv=None):
                     frac=round(cfg3["value"] / PEAK_BF16_TFLOPS, 4), steps=cfg3["steps"],
                     main_kernel_tflops=cfg3["roofline"]["achieved"],
                     main_kernel_frac=cfg3["roofline"]["frac"],
-                    per_projection_ms=cfg3["roofline"]["per_projection_ms"])
+                    per_projection_ms=cfg3["roofline"]["per_projection_ms"],
+                    per_projection_min_ms=cfg3["roofline"]["per_projection_min_ms"],
+                    clocks=cfg3["roofline"]["clocks"])
     st32 = (run_prefill(a, dev, hip, "stack32k", steps=a.stack_steps, warmup=1)
             if a.only in ("all", "stack32k") else None)
     if st32 is not None:
@@ -663,7 +733,9 @@ def main(argv=None):
                     value=round(st32["value"], 2), unit="TFLOP/s", frac=round(st32["value"] / PEAK_BF16_TFLOPS, 4),
                     steps=st32["steps"], calls_per_pass=st32["calls"],
                     main_kernel_tflops=st32["roofline"]["achieved"], main_kernel_frac=st32["roofline"]["frac"],
-                    per_projection_ms=st32["roofline"]["per_projection_ms"])
+                    per_projection_ms=st32["roofline"]["per_projection_ms"],
+                    per_projection_min_ms=st32["roofline"]["per_projection_min_ms"],
+                    clocks=st32["roofline"]["clocks"])
     decode = run_decode(a, dev, hip) if a.only in ("all", "decode") and not a.no_decode else None
     grouped = (run_decode(a, dev, hip, grouped=True)
                if a.only in ("all", "decode", "decode_grouped") and not a.no_decode else None)
