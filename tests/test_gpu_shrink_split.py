@@ -117,3 +117,20 @@ def test_split_shrink_gaussian(name):
         assert gates.explained_by_rounding(yn[over], ref[over], rep["rms"]).all()
     # the partials are summed in a fixed order: a second call gives the same bits
     assert np.array_equal(y_bits(y), y_bits(call(p, ranks, slices, "bf16")))
+
+
+def test_split_shrink_on_a_dirty_workspace():
+    """The ranked case (a rank-16 adapter whose second rank tile is skipped by the shrink and the
+    reduction alike) on a workspace whose bytes past the counter area are NaN before the call:
+    bitwise the same as on a fresh workspace, so no partial the call did not write is read."""
+    import torch
+    p, ranks, slices = problem("ranked", 73, integer=False)
+    X, W, A, B = to_device(p)
+    nbytes = bd.workspace_bytes(p.M, p.N, p.K, max(ranks), len(ranks))
+    ws = torch.full((nbytes,), 0xFF, dtype=torch.uint8, device="cuda")
+    ws[:bd.WORKSPACE_COUNTER_BYTES] = 0
+    y_dirty = bd.lora_proj_ranked(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, workspace=ws)
+    y_fresh = bd.lora_proj_ranked(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale)
+    torch.cuda.synchronize()
+    assert np.array_equal(y_bits(y_dirty), y_bits(y_fresh))
+    assert not np.isnan(y_to_numpy(y_dirty)).any()
