@@ -1031,15 +1031,16 @@ hipError_t launch_bf16_shrink(const ProjArgs& p, const SegTable& st, const Adapt
 int main_tile_rows(int M, int N) {
   // Blocks run one per CU in whole waves of the chip, so a call takes about
   // ceil(tiles / CUs) tile times.  A tile's time shrinks far less than its
-  // height, since the loop is bound per stage by its loads more than by its
-  // MFMAs: whole calls running a single wave of tiles took 1 : 0.90 : 0.83 for
-  // 256, 192 and 128 rows.  Take the height with the fewest tile times.
+  // height, since each stage's loads, LDS traffic and barrier do not shrink
+  // with it: whole calls running a single wave of tiles took about
+  // 1 : 0.88 : 0.77 for 256, 192 and 128 rows.  Take the height with the
+  // fewest tile times.
   constexpr int kCUs = 256;
   const int ntn = (N + 255) / 256;
   int best = 256;
   double best_cost = 0;
   for (const int tm : {256, 192, 128}) {
-    const double tile_time = tm == 256 ? 1.0 : tm == 192 ? 0.90 : 0.83;
+    const double tile_time = tm == 256 ? 1.0 : tm == 192 ? 0.88 : 0.77;
     const int64_t tiles = int64_t(ntn) * ((M + tm - 1) / tm);
     const double cost = double((tiles + kCUs - 1) / kCUs) * tile_time;
     if (tm == 256 || cost < best_cost) {
