@@ -9,7 +9,12 @@ Each case draws its own shape and call:
 - 1 to 6 adapters at one rank or each at its own (16 to 512), power-of-two scales of either sign;
 - a segment table of random lengths (empty segments included) naming any adapter or none.
 Inputs are integers in -2..2, so every partial sum is an integer below 2^24: the fp32 store must
-equal the exact result bit for bit and the bf16 store must be its correct rounding."""
+equal the exact result bit for bit and the bf16 store must be its correct rounding.
+
+A second sweep does the same for calls with 4-bit base weights (K a multiple of 128, one rank
+for every adapter): random codes and zero points with power-of-two group scales from 2^-5 to
+2^-1, so every dequantized weight is exact in bf16 and every partial sum is a multiple of 2^-5
+below 2^19, again exact in fp32."""
 from __future__ import annotations
 
 import numpy as np
@@ -17,7 +22,7 @@ import pytest
 
 import gates
 from gpu_util import log, to_device, y_bits, y_to_numpy
-from oracle import lora_proj_ref, lora_proj_sliced_ref
+from oracle import lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref
 from rank_adapted_gemm_amd import binding as bd
 from rank_adapted_gemm_amd import synth
 
@@ -131,3 +136,104 @@ def test_random_sweep_covers_its_features():
         seen["several"] += len({a for a in lab if a >= 0}) > 1
     assert all(v >= 2 for v in seen.values()), seen
     assert heights == {128, 192, 256}, heights
+
+
+# ------------------------------------------------------------------ 4-bit base weights
+N_Q4_CASES = 24
+Q4_SCALES = (0.5, 0.25, -0.5, 0.125, -0.25)
+
+
+def q4_case(i):
+    """The i-th 4-bit call of the sweep (seeded, host only)."""
+    g = np.random.Generator(np.random.PCG64(9500 + i))
+    kind = g.random()
+    large = kind >= 0.85
+    if kind < 0.4:
+        M = int(g.integers(1, 129))
+    else:
+        M = int(g.integers(2000, 3001)) if large else int(g.integers(129, 901))
+    K = 128 * int(g.integers(1, 10))
+    if g.random() < 0.3:
+        widths = [256 * int(g.integers(3, 6) if large else g.integers(1, 3)) for _ in range(int(g.integers(2, 5)))]
+    else:
+        widths = None
+    N = sum(widths) if widths else int(g.integers(3000, 4001) if large else g.integers(1, 1101))
+    n_ad = int(g.integers(1, 5))
+    # base terms |x w| <= 2 * 7.5 sum to at most 15 K, the expand to 8 |s| r K; all multiples of
+    # 2^-5, so exact in fp32 below 2^19
+    rmax = max(r for r in RANKS if 15 * K + 8 * 0.5 * r * K < 2 ** 19)
+    rank = int(g.choice([r for r in RANKS if r <= rmax]))
+    scales = [float(g.choice(Q4_SCALES)) for _ in range(n_ad)]
+    starts, labels = [0], []
+    while starts[-1] < M:
+        n = 0 if g.random() < 0.05 else int(g.integers(1, max(2, M // 3 + 1)))
+        starts.append(min(M, starts[-1] + n))
+        labels.append(int(g.integers(-1, n_ad)))
+    return dict(M=M, N=N, K=K, widths=widths, rank=rank, n_ad=n_ad, scales=scales, seg_starts=starts,
+                seg_adapter=labels)
+
+
+def q4_problem(i):
+    c = q4_case(i)
+    S = len(c["widths"]) if c["widths"] else 1
+    p = synth.random_problem(9500 + i, M=c["M"], N=c["N"], K=c["K"], rank=c["rank"], integer=True,
+                             ranks=[c["rank"]] * c["n_ad"], n_adapters=c["n_ad"], slices=S, scale=c["scales"],
+                             seg_starts=c["seg_starts"], seg_adapter=c["seg_adapter"])
+    g = np.random.Generator(np.random.PCG64(9700 + i))
+    N, K = c["N"], c["K"]
+    codes = g.integers(0, 16, size=(N, K)).astype(np.uint8)
+    zeros = g.integers(0, 16, size=(N, K // 128)).astype(np.uint32)
+    gscale = np.ldexp(1.0, g.integers(-5, 0, size=(N, K // 128))).astype(np.float32)
+    packed = (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+    params = (synth.f32_to_bf16_bits(gscale).astype(np.uint32) | (zeros << 16)).T.copy()
+    return c, p, packed, params
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_Q4_CASES))
+def test_random_q4_call_exact(i):
+    import torch
+    c, p, packed, params = q4_problem(i)
+    log(f"case random q4 {i}: M={c['M']} N={c['N']} K={c['K']} slices={c['widths']} rank={c['rank']} "
+        f"adapters={c['n_ad']} segments={len(c['seg_adapter'])} path={bd.path(c['M'], c['N'], c['K'], c['rank'])}")
+    exact = lora_proj_q4_ref(p.X, p.seg_starts, p.seg_adapter, packed, params, p.A, p.B, p.scale,
+                             slice_n=c["widths"])
+    assert np.all(np.abs(exact) * 32 < 2 ** 24)
+    X, _, A, B = to_device(p)
+    Wq = torch.from_numpy(np.ascontiguousarray(packed)).to("cuda")
+    Wp = torch.from_numpy(np.ascontiguousarray(params).view(np.int32)).to("cuda")
+
+    def run(dtype):
+        y = bd.lora_proj_q4(X, list(p.seg_starts), list(p.seg_adapter), Wq, Wp, A, B, c["scales"], dtype=dtype,
+                            slices=c["widths"])
+        torch.cuda.synchronize()
+        return y
+
+    y32 = y_to_numpy(run("bf16_f32out"))
+    bad = np.argwhere(y32 != exact)
+    assert bad.size == 0, f"{len(bad)} mismatches, first {bad[:5].tolist()}"
+    assert np.array_equal(y_bits(run("bf16")), gates.bf16_rne_of_f64(exact))
+
+
+def test_random_q4_sweep_covers_its_features():
+    """Host only: the 4-bit sweep's calls are valid and reach both paths, several tile heights,
+    slices, several adapters, empty segments and base rows."""
+    seen = dict(decode=0, prefill=0, sliced=0, empty=0, base=0, several=0)
+    heights = set()
+    for i in range(N_Q4_CASES):
+        c = q4_case(i)
+        M, N, K, r = c["M"], c["N"], c["K"], c["rank"]
+        assert K % 128 == 0 and 16 <= r <= 512 and r % 16 == 0
+        assert 15 * K + 8 * max(abs(v) for v in Q4_SCALES) * r * K < 2 ** 19
+        st, lab = c["seg_starts"], c["seg_adapter"]
+        assert st[0] == 0 and st[-1] == M and len(lab) == len(st) - 1
+        path = bd.path(M, N, K, r)
+        seen[path] += 1
+        if path == "prefill":
+            heights.add(bd.tile_rows(M, N, K))
+        seen["sliced"] += c["widths"] is not None
+        seen["empty"] += any(a == b for a, b in zip(st, st[1:]))
+        seen["base"] += -1 in lab
+        seen["several"] += len({a for a in lab if a >= 0}) > 1
+    assert all(v >= 2 for v in seen.values()), seen
+    assert len(heights) >= 2, heights
