@@ -14,7 +14,8 @@ equal the exact result bit for bit and the bf16 store must be its correct roundi
 A second sweep does the same for calls with 4-bit base weights (K a multiple of 128, one rank
 for every adapter): random codes and zero points with power-of-two group scales from 2^-5 to
 2^-1, so every dequantized weight is exact in bf16 and every partial sum is a multiple of 2^-5
-below 2^19, again exact in fp32."""
+below 2^19, again exact in fp32.  A third runs the fp32 test mode (fp32 inputs and arithmetic)
+on Gaussian inputs of random shapes, ranks, slices and tables against the 1e-5 rms bound."""
 from __future__ import annotations
 
 import numpy as np
@@ -237,3 +238,33 @@ def test_random_q4_sweep_covers_its_features():
         seen["several"] += len({a for a in lab if a >= 0}) > 1
     assert all(v >= 2 for v in seen.values()), seen
     assert len(heights) >= 2, heights
+
+
+# ------------------------------------------------------------------ fp32 test mode
+N_F32_CASES = 16
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_F32_CASES))
+def test_random_f32_call(i):
+    """The i-th call of the first sweep at its own shape and table (M capped at 600, N at 700),
+    in fp32 with Gaussian inputs and scales: within 1e-5 rms of the oracle."""
+    import torch
+    c = case(i)
+    M = min(c["M"], 600)
+    starts = [min(v, M) for v in c["seg_starts"]]
+    widths = None if c["widths"] is None else [256] * min(len(c["widths"]), 2)
+    N = sum(widths) if widths else min(c["N"], 700)
+    S = len(widths) if widths else 1
+    scales = [0.7 * v for v in c["scales"]]
+    p = synth.random_problem(9800 + i, M=M, N=N, K=c["K"], rank=c["ranks"][0], dtype="f32", ranks=c["ranks"],
+                             n_adapters=len(c["ranks"]), slices=S, scale=scales, seg_starts=starts,
+                             seg_adapter=c["seg_adapter"])
+    log(f"case random f32 {i}: M={M} N={N} K={c['K']} slices={widths} ranks={c['ranks']} ranked={c['ranked']}")
+    ref = (lora_proj_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale) if widths is None else
+           lora_proj_sliced_ref(p.X, p.seg_starts, p.seg_adapter, p.W, p.A, p.B, p.scale, widths))
+    X, W, A, B = to_device(p)
+    entry = bd.lora_proj_ranked if c["ranked"] else bd.lora_proj
+    y = entry(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, scales, dtype="f32", slices=widths)
+    torch.cuda.synchronize()
+    assert gates.passes_f32(y_to_numpy(y), ref), gates.report(y_to_numpy(y), ref)
