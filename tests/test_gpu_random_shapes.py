@@ -14,15 +14,17 @@ equal the exact result bit for bit and the bf16 store must be its correct roundi
 A second sweep does the same for calls with 4-bit base weights (K a multiple of 128, one rank
 for every adapter): random codes and zero points with power-of-two group scales from 2^-5 to
 2^-1, so every dequantized weight is exact in bf16 and every partial sum is a multiple of 2^-5
-below 2^19, again exact in fp32.  A third runs the fp32 test mode (fp32 inputs and arithmetic)
-on Gaussian inputs of random shapes, ranks, slices and tables against the 1e-5 rms bound."""
+below 2^19, again exact in fp32.  Two more take the first sweep's calls on Gaussian inputs: in
+bf16 against the rounding-aware G2 bound (and every element past the literal G1 bound must be
+the correct bf16 rounding of the oracle value), and in the fp32 test mode (fp32 inputs and
+arithmetic) against the 1e-5 rms bound."""
 from __future__ import annotations
 
 import numpy as np
 import pytest
 
 import gates
-from gpu_util import log, to_device, y_bits, y_to_numpy
+from gpu_util import log, record, to_device, y_bits, y_to_numpy
 from oracle import lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref
 from rank_adapted_gemm_amd import binding as bd
 from rank_adapted_gemm_amd import synth
@@ -137,6 +139,33 @@ def test_random_sweep_covers_its_features():
         seen["several"] += len({a for a in lab if a >= 0}) > 1
     assert all(v >= 2 for v in seen.values()), seen
     assert heights == {128, 192, 256}, heights
+
+
+N_GAUSS_CASES = 24
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("i", range(N_GAUSS_CASES))
+def test_random_call_gaussian(i):
+    """The i-th call of the sweep on Gaussian inputs (the workloads' sigmas) and scales of mixed
+    sign: G2 against the oracle, and past the literal G1 bound only correct roundings."""
+    c = case(i)
+    S = len(c["widths"]) if c["widths"] else 1
+    scales = [0.7 * v for v in c["scales"]]
+    p = synth.random_problem(9900 + i, M=c["M"], N=c["N"], K=c["K"], rank=c["ranks"][0], ranks=c["ranks"],
+                             n_adapters=len(c["ranks"]), slices=S, scale=scales, seg_starts=c["seg_starts"],
+                             seg_adapter=c["seg_adapter"])
+    c = dict(c, scales=scales)
+    log(f"case random gaussian {i}: M={c['M']} N={c['N']} K={c['K']} slices={c['widths']} ranks={c['ranks']}")
+    ref = exact_of(c, p)
+    y = y_to_numpy(call(c, p, to_device(p), "bf16"))
+    rep = gates.report(y, ref)
+    over = np.abs(y - ref) > gates.BF16_TOL * rep["rms"]
+    log(f"  rms={rep['rms']:.4g} G1={rep['g1']:.3e} G2={rep['g2']:.3e} past-G1={int(over.sum())}")
+    record(f"random/{i}", rep, int(over.sum()))
+    assert rep["nonfinite"] == 0 and rep["g2"] <= gates.BF16_TOL, rep
+    if over.any():
+        assert gates.explained_by_rounding(y[over], ref[over], rep["rms"]).all()
 
 
 # ------------------------------------------------------------------ 4-bit base weights
