@@ -1,7 +1,8 @@
 """lora_proj_noalloc, the entry point that allocates nothing, through the C-ABI: two calls in a
 row, the second with a smaller input, each bitwise equal to lora_proj's result on the same
 inputs (the same kernels run; only the workspace differs); a decode call after a prefill call
-sees clean counters; a call whose scratch would exceed the fixed array is refused."""
+sees clean counters; the random sweep's shapes and tables back to back on the one array; a call
+whose scratch would exceed the fixed array is refused."""
 from __future__ import annotations
 
 import numpy as np
@@ -69,6 +70,32 @@ def test_noalloc_repeated_decode_calls_stay_exact():
         bd.lora_proj_noalloc(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, out, dtype="bf16_f32out")
         torch.cuda.synchronize()
         assert np.array_equal(y_to_numpy(out), exact)
+
+
+def test_noalloc_random_calls_in_a_row():
+    """The random sweep's shapes and segment tables (one rank, the largest of each call's, and one
+    scale; no slices, which this entry point does not take) back to back on the one array, decode
+    and prefill calls of every size in turn: each bitwise equal to lora_proj on the same inputs."""
+    import torch
+    from test_gpu_random_shapes import N_CASES, case
+    ran = 0
+    for i in range(N_CASES):
+        c = case(i)
+        N = sum(c["widths"]) if c["widths"] else c["N"]
+        r, n_ad = max(c["ranks"]), len(c["ranks"])
+        if bd.workspace_bytes(c["M"], N, c["K"], r, n_ad) > bd.NOALLOC_SCRATCH_BYTES:
+            continue
+        p = synth.random_problem(9600 + i, M=c["M"], N=N, K=c["K"], rank=r, n_adapters=n_ad, scale=0.75,
+                                 seg_starts=c["seg_starts"], seg_adapter=c["seg_adapter"])
+        log(f"case noalloc random {i} M={p.M} N={N} K={p.K} r={r} path={bd.path(p.M, N, p.K, r)}")
+        X, W, A, B = to_device(p)
+        ref = bd.lora_proj(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale)
+        out = torch.full((p.M, N), float("nan"), dtype=torch.bfloat16, device="cuda")
+        y = bd.lora_proj_noalloc(X, list(p.seg_starts), list(p.seg_adapter), W, A, B, p.scale, out)
+        torch.cuda.synchronize()
+        assert np.array_equal(y_bits(y), y_bits(ref)), i
+        ran += 1
+    assert ran >= 40, ran
 
 
 def test_noalloc_refuses_scratch_past_the_array():
