@@ -29,7 +29,7 @@ from oracle import lora_proj_q4_ref, lora_proj_ref, lora_proj_sliced_ref
 from rank_adapted_gemm_amd import binding as bd
 from rank_adapted_gemm_amd import synth
 
-N_CASES = 48
+N_CASES = 96
 RANKS = (16, 32, 48, 64, 96, 128, 256, 512)
 SCALES = (1.0, 0.5, -2.0, 0.25, -1.0)
 
@@ -169,7 +169,7 @@ def test_random_call_gaussian(i):
 
 
 # ------------------------------------------------------------------ 4-bit base weights
-N_Q4_CASES = 24
+N_Q4_CASES = 40
 Q4_SCALES = (0.5, 0.25, -0.5, 0.125, -0.25)
 
 
